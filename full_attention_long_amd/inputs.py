@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no arithmetic of the method: it only draws random numbers and fixes
+workload shapes.  Both the HIP path and the oracle receive the exact bytes made here.
+
+Seed scheme: workload k draws stream s from ``torch.Generator().manual_seed(1000*k + s)``.
+Streams: 0 Q, 1 K, 2 V, 3 key states, 4 W1, 5 W2, 6 routing bits, 7 sequence lengths,
+8 sampled query rows.  Values are ``randn`` in fp32, rounded to bf16 with
+round-to-nearest-even by ``Tensor.to(torch.bfloat16)`` where the workload is bf16.
+
+The workloads stand in for the pages' long-context evaluations (LongBench-E/V2 and RULER
+up to 256K tokens, Elastic Attention blog post section 4); their sparse-head ratios follow
+the per-task ratios the post reports for its Figure 6 (about 85% for code, 68% for QA).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_KS, STREAM_W1, STREAM_W2 = 0, 1, 2, 3, 4, 5
+STREAM_ROUTE, STREAM_LENS, STREAM_ROWS = 6, 7, 8
+
+
+def seed(workload: int, stream: int) -> int:
+    return 1000 * workload + stream
+
+
+def gen(workload: int, stream: int) -> torch.Generator:
+    return torch.Generator().manual_seed(seed(workload, stream))
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic prefill layer."""
+    index: int                      # k in the seed scheme
+    name: str
+    dtype: torch.dtype
+    n_heads_q: int
+    n_heads_kv: int
+    head_dim: int
+    sink: int
+    window: int
+    lengths: tuple = ()             # fixed lengths; empty -> drawn (ragged)
+    ragged_count: int = 0
+    ragged_range: tuple = (0, 0)
+    p_sparse: float = 0.0           # Bernoulli routing (ignored when fixed_route/router)
+    fixed_route: tuple = ()         # explicit route for batch 1
+    router: bool = False            # routing bits come from the Attention Router
+    router_hidden: int = 256
+    router_w_std: float = 0.02
+    sampled_rows: int = 0           # 0 -> oracle evaluates every row
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    # tiny fp32 correctness case: 1 x 512, 4 q heads on 2 KV heads, D=64, r=[0,1,0,1]
+    "tiny_fp32": Workload(1, "tiny_fp32", torch.float32, 4, 2, 64, 16, 64,
+                          lengths=(512,), fixed_route=(0, 1, 0, 1)),
+    # Llama-3.1-8B-shaped layer at 8K, Bernoulli(0.7) sparse heads, sink 128, window 1024
+    "llama8b_8k": Workload(2, "llama8b_8k", torch.bfloat16, 32, 8, 128, 128, 1024,
+                           lengths=(8192,), p_sparse=0.7),
+    # Qwen3-8B-shaped layer at 32K, routing from the Attention Router (27/32 sparse),
+    # sink 128, window 2048
+    "qwen3_8b_32k": Workload(3, "qwen3_8b_32k", torch.bfloat16, 32, 8, 128, 128, 2048,
+                             lengths=(32768,), router=True, sampled_rows=2048),
+    # ragged batch of 4, lengths U[4096, 32768], Bernoulli(0.68), sink 64, window 1024
+    "ragged4": Workload(4, "ragged4", torch.bfloat16, 32, 8, 128, 64, 1024,
+                        ragged_count=4, ragged_range=(4096, 32768), p_sparse=0.68,
+                        sampled_rows=2048),
+    # long context 256K, Bernoulli(0.8), sink 128, window 4096
+    "long_256k": Workload(5, "long_256k", torch.bfloat16, 32, 8, 128, 128, 4096,
+                          lengths=(262144,), p_sparse=0.8, sampled_rows=2048),
+}
+
+
+def lengths(w: Workload) -> list:
+    if w.lengths:
+        return list(w.lengths)
+    lo, hi = w.ragged_range
+    g = gen(w.index, STREAM_LENS)
+    return [int(x) for x in torch.randint(lo, hi + 1, (w.ragged_count,), generator=g)]
+
+
+def cu_seqlens(lens) -> torch.Tensor:
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + int(n))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def normal(shape, workload: int, stream: int, dtype: torch.dtype, std: float = 1.0,
+           chunk_rows: int = 16384) -> torch.Tensor:
+    """randn(shape) * std from the (workload, stream) generator, drawn in chunks of
+    ``chunk_rows`` along dim 0 (bounded fp32 temporaries), then cast to ``dtype``."""
+    g = gen(workload, stream)
+    out = torch.empty(shape, dtype=dtype)
+    n0 = shape[0]
+    for a in range(0, n0, chunk_rows):
+        b = min(n0, a + chunk_rows)
+        x = torch.randn((b - a,) + tuple(shape[1:]), generator=g, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[a:b] = x.to(dtype)
+    return out
+
+
+def qkv(w: Workload, total_tokens: int):
+    """Q [T, Hq, D], K [T, Hkv, D], V [T, Hkv, D] on the CPU."""
+    q = normal((total_tokens, w.n_heads_q, w.head_dim), w.index, STREAM_Q, w.dtype)
+    k = normal((total_tokens, w.n_heads_kv, w.head_dim), w.index, STREAM_K, w.dtype)
+    v = normal((total_tokens, w.n_heads_kv, w.head_dim), w.index, STREAM_V, w.dtype)
+    return q, k, v
+
+
+def bernoulli_route(w: Workload, batch: int) -> torch.Tensor:
+    """uint8 [batch, Hq]; 1 (sparse) with probability p_sparse, i.i.d."""
+    if w.fixed_route:
+        return torch.tensor([list(w.fixed_route)] * batch, dtype=torch.uint8)
+    g = gen(w.index, STREAM_ROUTE)
+    return (torch.rand((batch, w.n_heads_q), generator=g) < w.p_sparse).to(torch.uint8)
+
+
+def router_weights(w: Workload):
+    """Router parameters with the bias-free second layer: W1 [hidden, Hkv*D] and
+    W2 [Hq, hidden] ~ N(0, std^2) fp32, b1 = 0, b2 = 0.  The output bias that sets the
+    sparse ratio is a stored fixture (tests/golden), written from the oracle."""
+    c = w.n_heads_kv * w.head_dim
+    w1 = normal((w.router_hidden, c), w.index, STREAM_W1, torch.float32, std=w.router_w_std)
+    w2 = normal((w.n_heads_q, w.router_hidden), w.index, STREAM_W2, torch.float32,
+                std=w.router_w_std)
+    b1 = torch.zeros(w.router_hidden, dtype=torch.float32)
+    b2 = torch.zeros(w.n_heads_q, dtype=torch.float32)
+    return w1, b1, w2, b2
+
+
+def sampled_rows(w: Workload, lens, per_seq: int, bm: int = 128) -> torch.Tensor:
+    """Packed token indices to check: for every sequence the boundary positions
+    (0, 1, sink-1, sink, window-1, window, sink+window-2, sink+window-1, L-1 and the
+    rows on both sides of a few q-tile edges) plus uniform draws without replacement,
+    ``per_seq`` rows in all per sequence (fewer when the sequence is shorter)."""
+    g = gen(w.index, STREAM_ROWS)
+    out = []
+    start = 0
+    for n in lens:
+        n = int(n)
+        fixed = {0, 1, w.sink - 1, w.sink, w.window - 1, w.window,
+                 w.sink + w.window - 2, w.sink + w.window - 1, n - 1}
+        for t in (1, 2, 7, n // (2 * bm), n // bm - 1):
+            fixed.update({t * bm - 1, t * bm})
+        fixed = sorted(x for x in fixed if 0 <= x < n)
+        want = min(per_seq, n)
+        fixed_set = set(fixed)
+        rest = [x for x in torch.randperm(n, generator=g).tolist() if x not in fixed_set]
+        pick = sorted(fixed_set | set(rest[: max(0, want - len(fixed))]))
+        out.extend(start + x for x in pick)
+        start += n
+    return torch.tensor(out, dtype=torch.int64)

@@ -1,0 +1,52 @@
+"""Work counts used to report effective throughput.
+
+Effective FLOPs count only the (query, key) score positions the mask keeps: each kept
+position costs 2*D FLOPs in Q K^T and 2*D in P V, i.e. 4*D in all.  Masked positions that
+a tiled kernel still computes are not counted.
+
+Visible keys of row i (0-based) of one sequence:
+  full head (r = 0):     i + 1
+  sparse head (r = 1):   min(i+1, W) window keys plus min(s, i-W+1) sink keys that the
+                         window does not already cover (when i-W+1 > 0).
+Summed over the L rows of a sequence:
+  full:   L(L+1)/2
+  sparse: window part L(L+1)/2 if L <= W else W(W+1)/2 + (L-W)W;
+          sink part with n = L-W: 0 if n <= 0, n(n+1)/2 if n <= s, else s(s+1)/2 + (n-s)s.
+"""
+from __future__ import annotations
+
+
+def visible_pairs(length: int, sparse: bool, sink: int, window: int) -> int:
+    L, s, W = int(length), int(sink), int(window)
+    if L <= 0:
+        return 0
+    if not sparse:
+        return L * (L + 1) // 2
+    win = L * (L + 1) // 2 if L <= W else W * (W + 1) // 2 + (L - W) * W
+    n = L - W
+    if n <= 0:
+        snk = 0
+    elif n <= s:
+        snk = n * (n + 1) // 2
+    else:
+        snk = s * (s + 1) // 2 + (n - s) * s
+    return win + snk
+
+
+def effective_flops(lengths, route, head_dim: int, sink: int, window: int) -> int:
+    """Sum over sequences b and query heads h of 4*D*visible_pairs(L_b, route[b][h])."""
+    total = 0
+    for b, L in enumerate(lengths):
+        for r in route[b]:
+            total += 4 * int(head_dim) * visible_pairs(L, bool(int(r)), sink, window)
+    return total
+
+
+def io_bytes(total_tokens: int, n_heads_q: int, n_heads_kv: int, head_dim: int,
+             elem_bytes: int) -> int:
+    """Algorithmic HBM bytes of one attention launch: Q, K, V read once, O written once."""
+    return int(total_tokens) * int(head_dim) * int(elem_bytes) * (2 * n_heads_q + 2 * n_heads_kv)
+
+
+MI355X_BF16_DENSE_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense (no sparsity)
+MI355X_HBM_GBPS = 8000.0

@@ -1,0 +1,181 @@
+"""Oracle for the routed hybrid-attention prefill -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow fp64 CPU reference.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product library never does, and
+this package imports nothing from the product package.
+
+The arithmetic lives in ``ea_oracle.c`` (fp64, OpenMP); this module compiles it with gcc
+and marshals arguments through ctypes.  The C header comment lists the pages each
+function follows (Elastic Attention blog post, section 2.1 "Attention Router",
+section 1 and section 3 "Fused Kernel"; gist.science explanation, section "问题所在")
+and the readings taken where the pages are silent.
+
+Functions:
+  attn(...)      masked-softmax attention over explicit per-head visible sets
+  route(...)     mean-pool -> MLP (SiLU) -> logits -> hard threshold
+  worklist(...)  (seq, head, q_tile, cost) items, longest first
+  build()        compile the C oracle (gcc -O2 -fopenmp)
+
+Parity pins for every function are in tests/test_oracle.py (brute force, closed forms,
+identities, library special cases, hand-derived router fixture).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ea_oracle.c")
+_LIB = os.path.join(_HERE, "libea_oracle.so")
+_lib = None
+
+_DT_BF16, _DT_F32, _DT_F64 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile ea_oracle.c into oracle/libea_oracle.so with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_attn.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, P, i32, i32, dbl,
+                                    P, i64, P, P, i32]
+        lib.oracle_attn.restype = i32
+        lib.oracle_route.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P]
+        lib.oracle_route.restype = i32
+        lib.oracle_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i64,
+                                        ctypes.POINTER(i64)]
+        lib.oracle_worklist.restype = i32
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _as_elements(x):
+    """Return (contiguous numpy array holding the exact stored bits, dtype code)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy(), _DT_BF16
+            if x.dtype == torch.float32:
+                return x.numpy(), _DT_F32
+            if x.dtype == torch.float64:
+                return x.numpy(), _DT_F64
+            raise TypeError(f"unsupported tensor dtype {x.dtype}")
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, _DT_F32
+    if x.dtype == np.float64:
+        return x, _DT_F64
+    raise TypeError(f"unsupported array dtype {x.dtype}")
+
+
+def _np(x, dtype):
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=dtype))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def attn(q, k, v, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window, scale=None,
+         rows=None, nthreads=0):
+    """fp64 routed attention.  q [T, Hq, D], k/v [T, Hkv, D] (bf16, fp32 or fp64; all
+    three the same dtype), cu_seqlens [B+1], route [B, Hq] (0 full, 1 sparse).
+    rows: packed token indices to evaluate (None = all).
+    Returns (o [n_rows, Hq, D] float64, lse [n_rows, Hq] float64)."""
+    lib = _load()
+    qa, dt = _as_elements(q)
+    ka, dtk = _as_elements(k)
+    va, dtv = _as_elements(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share one dtype")
+    d = int(qa.shape[-1])
+    cu = _np(cu_seqlens, np.int32)
+    batch = int(cu.shape[0] - 1)
+    r = _np(route, np.uint8).reshape(batch, n_heads_q)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if rows is None:
+        rows_arr, n_rows = None, int(cu[-1])
+    else:
+        rows_arr = _np(rows, np.int64).reshape(-1)
+        n_rows = int(rows_arr.shape[0])
+    o = np.empty((n_rows, n_heads_q, d), dtype=np.float64)
+    lse = np.empty((n_rows, n_heads_q), dtype=np.float64)
+    rc = lib.oracle_attn(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                         cu.ctypes.data, batch, n_heads_q, n_heads_kv, d,
+                         r.ctypes.data, int(sink), int(window), float(scale),
+                         None if rows_arr is None else rows_arr.ctypes.data, n_rows,
+                         o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn failed with code {rc}")
+    return o, lse
+
+
+def route(key_states, cu_seqlens, w1, b1, w2, b2):
+    """fp64 Attention Router.  key_states [T, C] (bf16/fp32/fp64), w1 [H, C], b1 [H],
+    w2 [Hq, H], b2 [Hq] (fp32).  Returns (pooled [B, C], logits [B, Hq], r [B, Hq] uint8)."""
+    lib = _load()
+    ks, dt = _as_elements(key_states)
+    kv_dim = int(ks.shape[-1])
+    cu = _np(cu_seqlens, np.int32)
+    batch = int(cu.shape[0] - 1)
+    w1a, b1a = _np(w1, np.float32), _np(b1, np.float32)
+    w2a, b2a = _np(w2, np.float32), _np(b2, np.float32)
+    hidden, n_heads = int(w1a.shape[0]), int(w2a.shape[0])
+    pooled = np.empty((batch, kv_dim), dtype=np.float64)
+    logits = np.empty((batch, n_heads), dtype=np.float64)
+    r = np.empty((batch, n_heads), dtype=np.uint8)
+    rc = lib.oracle_route(ks.ctypes.data, dt, kv_dim, cu.ctypes.data, batch,
+                          w1a.ctypes.data, b1a.ctypes.data, hidden,
+                          w2a.ctypes.data, b2a.ctypes.data, n_heads,
+                          pooled.ctypes.data, logits.ctypes.data, r.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_route failed with code {rc}")
+    return pooled, logits, r
+
+
+def worklist(route, cu_seqlens, n_heads_q, sink, window, bm, bn):
+    """Sorted work items int32 [N, 4] = (seq, head, q_tile, cost)."""
+    lib = _load()
+    cu = _np(cu_seqlens, np.int32)
+    batch = int(cu.shape[0] - 1)
+    r = _np(route, np.uint8).reshape(batch, n_heads_q)
+    n = ctypes.c_int64(0)
+    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, batch, n_heads_q, int(sink),
+                             int(window), int(bm), int(bn), None, 0, ctypes.byref(n))
+    if rc != 0:
+        raise ValueError(f"oracle_worklist failed with code {rc}")
+    items = np.empty((max(n.value, 1), 4), dtype=np.int32)
+    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, batch, n_heads_q, int(sink),
+                             int(window), int(bm), int(bn), items.ctypes.data, n.value,
+                             ctypes.byref(n))
+    if rc != 0:
+        raise ValueError(f"oracle_worklist failed with code {rc}")
+    return items[: n.value]
