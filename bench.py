@@ -1,0 +1,229 @@
+"""Benchmark of the routed hybrid-attention prefill layer on one MI355X.
+
+One step = the whole hot path of one layer on resident inputs:
+  ea_route (mean-pool + router MLP + threshold) -> ea_hybrid_attn_prefill (work-list
+  planner + persistent fused attention), for the Qwen3-8B-shaped layer at 32K tokens
+  (32 query / 8 KV heads, head_dim 128, bf16, sink 128, window 2048, 27 of 32 heads sparse
+  by the router).
+
+Prints ONE JSON line: effective TFLOP/s (only unmasked score positions count, 4*D FLOPs
+each), ms per layer, % of the bf16 dense MFMA peak, the roofline of the attention kernel
+(timed with HIP events on the launch stream) and the fp64 oracle's throughput on a bounded
+sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
+
+METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
+GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Resident device buffers of one synthetic layer."""
+
+    def __init__(self, name: str):
+        w = inputs.WORKLOADS[name]
+        self.w = w
+        self.lens = inputs.lengths(w)
+        T = sum(self.lens)
+        self.T = T
+        dev = torch.device("cuda:0")
+        q, k, v = inputs.qkv(w, T)
+        self.cpu = (q, k, v)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.cu_host = inputs.cu_seqlens(self.lens)
+        self.cu = self.cu_host.to(dev)
+        self.max_len = max(self.lens)
+        B, hq = len(self.lens), w.n_heads_q
+        self.route = torch.empty(B, hq, dtype=torch.uint8, device=dev)
+        if w.router:
+            w1, b1, w2, b2 = inputs.router_weights(w)
+            with open(GOLDEN_BIAS) as f:
+                b2 = torch.full_like(b2, json.load(f)["b2"])
+            self.router = [t.to(dev) for t in (w1, b1, w2, b2)]
+            self.ks = self.k.view(T, w.n_heads_kv * w.head_dim)
+            kv_dim, hidden = self.ks.shape[1], w1.shape[0]
+        else:
+            self.router = None
+            self.route.copy_(inputs.bernoulli_route(w, B))
+            kv_dim = hidden = 0
+        self.ws = torch.empty(ea.workspace_size(B, self.max_len, hq, kv_dim, hidden),
+                              dtype=torch.uint8, device=dev)
+        bm, _ = ea.tile_config(ea.EA_BF16, w.head_dim)
+        self.wl = torch.empty(B * hq * -(-self.max_len // bm), 4, dtype=torch.int32, device=dev)
+        self.n_items = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def do_route(self):
+        if self.router is not None:
+            w1, b1, w2, b2 = self.router
+            ea.route(self.ks, self.cu, w1, b1, w2, b2, self.route, self.ws)
+
+    def do_plan(self):
+        w = self.w
+        ea.build_worklist(self.route, self.cu, self.max_len, w.n_heads_q, w.sink, w.window,
+                          ea.EA_BF16, w.head_dim, self.wl, self.ws, n_items_out=self.n_items,
+                          want_count=False)
+
+    def do_attn(self):
+        w = self.w
+        ea.hybrid_attn_run(self.q, self.k, self.v, self.o, self.cu, self.max_len, self.route,
+                           w.sink, w.window, self.wl, self.n_items, self.ws)
+
+    def step(self):
+        """One layer: router, then the fused prefill (planner + attention)."""
+        w = self.w
+        self.do_route()
+        ea.hybrid_attn_prefill(self.q, self.k, self.v, self.o, self.cu, self.max_len,
+                               self.route, w.sink, w.window, self.ws)
+
+    def flops(self):
+        r = self.route.cpu().tolist()
+        return metrics.effective_flops(self.lens, r, self.w.head_dim, self.w.sink, self.w.window)
+
+
+def time_events(fn, n):
+    """Average ms of fn() over n calls, HIP events on the current (launch) stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def cpu_baseline(layer: Layer, seconds: float):
+    """fp64 oracle on sampled query rows of the same workload, all host cores."""
+    import numpy as np
+    import oracle
+    w = layer.w
+    q, k, v = layer.cpu
+    route = layer.route.cpu().numpy()
+    g = torch.Generator().manual_seed(inputs.seed(w.index, inputs.STREAM_ROWS) + 7)
+    perm = torch.randperm(layer.T, generator=g).numpy()
+    cu = layer.cu_host.numpy()
+    done_rows, flops, t_used, at, batch = 0, 0, 0.0, 0, 8
+    threads = oracle.max_threads()
+    while t_used < seconds and at < layer.T:
+        rows = np.sort(perm[at:at + batch])
+        at += batch
+        t0 = time.perf_counter()
+        oracle.attn(q, k, v, cu, w.n_heads_q, w.n_heads_kv, route, w.sink, w.window, rows=rows)
+        t_used += time.perf_counter() - t0
+        for t in rows:
+            b = int(np.searchsorted(cu, t, side="right") - 1)
+            i = int(t - cu[b])
+            for h in range(w.n_heads_q):
+                if route[b, h]:
+                    n_vis = min(i + 1, w.window) + max(0, min(w.sink, i - w.window + 1))
+                else:
+                    n_vis = i + 1
+                flops += 4 * w.head_dim * n_vis
+        done_rows += len(rows)
+        batch = min(256, batch * 2)
+    tflops = flops / t_used / 1e12
+    full_layer_s = layer.flops() / (flops / t_used)
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_rows} uniformly drawn query rows x {w.n_heads_q} heads of the "
+                      f"same layer ({t_used:.1f} s of fp64 oracle work); full layer "
+                      f"extrapolated to {full_layer_s:.0f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the routed "
+                                   "prefill is not sharded across GPUs (--gpus 1)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    ea.lib()  # fail loudly if the HIP library is missing
+
+    layer = Layer(args.workload)
+    w = layer.w
+    log(f"workload {w.name}: lens={layer.lens} T={layer.T}")
+    layer.do_route()
+    torch.cuda.synchronize()
+    n_sparse = int(layer.route.sum().item())
+    F = layer.flops()
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_events(layer.step, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.3f} s)")
+
+    # phase breakdown and the attention kernel alone (same stream)
+    ms_route = time_events(layer.do_route, args.steps) if layer.router is not None else 0.0
+    ms_plan = time_events(layer.do_plan, args.steps)
+    layer.do_plan()
+    ms_attn = time_events(layer.do_attn, args.steps)
+    io = metrics.io_bytes(layer.T, w.n_heads_q, w.n_heads_kv, w.head_dim, 2)
+    attn_tflops = F / (ms_attn * 1e-3) / 1e12
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    value = F / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": len(layer.lens), "seq_len": layer.max_len,
+                   "total_tokens": layer.T, "n_heads_q": w.n_heads_q,
+                   "n_heads_kv": w.n_heads_kv, "head_dim": w.head_dim, "sink": w.sink,
+                   "window": w.window, "sparse_heads": n_sparse,
+                   "routing": "router" if w.router else f"bernoulli({w.p_sparse})"},
+        "pct_bf16_peak": round(100.0 * value / peak, 2),
+        "effective_tflop": round(F / 1e12, 4),
+        "ms_breakdown": {"route": round(ms_route, 4), "plan": round(ms_plan, 4),
+                         "attention": round(ms_attn, 4)},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128>",
+                     "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "algorithmic_bytes": io, "launch_ms": round(ms_attn, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        rec["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,366 @@
+// ea_api.hip -- host side of libea.so: the C ABI declared in include/ea.h.
+//
+// Every argument is checked here, on the host, before anything is enqueued, so a
+// rejected call launches nothing and leaves every output untouched.  The library never
+// allocates device memory: the router partial sums, the planner's cells and the work
+// list live in the caller's workspace, carved by ws_layout().
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/ea.h"
+#include "ea_internal.h"
+
+namespace ea {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ea_status fail(ea_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+
+ea_status hip_fail(hipError_t e, const char* where) {
+  return fail(EA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool tile_shape(ea_dtype dt, int32_t head_dim, int* bm, int* bn) {
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (dt == EA_BF16) {
+    *bm = kBf16BM;
+    *bn = kBf16BN;
+    return true;
+  }
+  if (dt == EA_F32) {
+    *bm = kF32BM;
+    *bn = kF32BN;
+    return true;
+  }
+  return false;
+}
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+
+hipError_t cu_count(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && g_cu_count[dev] > 0) {
+    *out = g_cu_count[dev];
+    return hipSuccess;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev] = n;
+  *out = n;
+  return hipSuccess;
+}
+
+// Checks shared by the attention entry points.  Fills bm/bn.
+ea_status check_attn_args(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+                          const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                          int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                          const uint8_t* route, int32_t sink, int32_t window, float scale,
+                          void* workspace, int* bm, int* bn) {
+  if (!q || !k || !v || !o || !cu_seqlens || !route || !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || max_seqlen < 0) return fail(EA_ERR_INVALID_ARG, "batch < 1 or max_seqlen < 0");
+  if (n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(EA_ERR_INVALID_ARG, "n_heads_q must be a positive multiple of n_heads_kv");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  if (isnan(scale) || isinf(scale)) return fail(EA_ERR_INVALID_ARG, "scale is not finite");
+  if (!tile_shape(dt, head_dim, bm, bn))
+    return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(EA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (o == q || o == k || o == v) return fail(EA_ERR_INVALID_ARG, "o aliases q, k or v");
+  const int64_t elem = dt == EA_BF16 ? 2 : 4;
+  // per-sequence K/V windows and per-item Q/O windows use 32-bit byte offsets
+  if ((int64_t)max_seqlen * n_heads_kv * head_dim * elem >= ((int64_t)1 << 31) ||
+      (int64_t)(*bm + 1) * n_heads_q * head_dim * elem >= ((int64_t)1 << 31))
+    return fail(EA_ERR_UNSUPPORTED, "sequence too long for 32-bit per-sequence addressing");
+  if (ceil_div64(max_seqlen, *bn) + 2 > kPlanMaxBins)
+    return fail(EA_ERR_UNSUPPORTED, "max_seqlen exceeds the planner's cost range");
+  return EA_OK;
+}
+
+ea_status check_cu_host(const int32_t* cu, int32_t batch, int32_t max_seqlen) {
+  if (cu[0] != 0) return fail(EA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)cu[b + 1] - cu[b];
+    if (len < 0) return fail(EA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing");
+    if (len > max_seqlen) return fail(EA_ERR_INVALID_ARG, "a sequence is longer than max_seqlen");
+  }
+  return EA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+ea_status enqueue_plan(const uint8_t* route, const int32_t* cu, int32_t batch,
+                       int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
+                       int bm, int bn, int4* items, int32_t* n_items_out, const WsLayout& L,
+                       char* ws, hipStream_t stream) {
+  PlanArgs p;
+  p.route = route;
+  p.cu = cu;
+  p.batch = batch;
+  p.n_heads_q = n_heads_q;
+  p.sink = sink;
+  p.window = window;
+  p.bm = bm;
+  p.bn = bn;
+  p.bins = (int)(ceil_div64(max_seqlen, bn) + 2);
+  p.qt_prefix = (int32_t*)(ws + L.qt_prefix);
+  p.n_sparse = (int32_t*)(ws + L.n_sparse);
+  p.cells = (int4*)(ws + L.cells);
+  p.sorted = (int4*)(ws + L.sorted);
+  p.cell_off = (int32_t*)(ws + L.cell_off);
+  p.items = items;
+  p.counters = (int32_t*)(ws + L.counters);
+  p.n_items_out = n_items_out;
+  hipError_t e = launch_plan(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "planner launch");
+  return EA_OK;
+}
+
+ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+                       const int32_t* cu, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
+                       int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window,
+                       float scale, float* lse, const int4* items, const int32_t* n_items,
+                       int32_t* queue, int grid_blocks, hipStream_t stream) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.cu = cu;
+  a.route = route;
+  a.items = items;
+  a.n_items = n_items;
+  a.queue = queue;
+  a.lse = lse;
+  a.batch = batch;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+  int grid = grid_blocks;
+  if (grid <= 0) {
+    int ncu = 0;
+    hipError_t e = cu_count(&ncu);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+    grid = ncu * (dt == EA_BF16 ? attn_bf16_blocks_per_cu() : attn_f32_blocks_per_cu());
+  }
+  hipError_t e = launch_reset_queue(queue, stream);
+  if (e != hipSuccess) return hip_fail(e, "queue reset launch");
+  e = dt == EA_BF16 ? launch_attn_bf16(a, grid, stream) : launch_attn_f32(a, grid, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return EA_OK;
+}
+
+}  // namespace
+
+bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
+               int32_t hidden, WsLayout* out) {
+  if (batch < 1 || max_seqlen < 0 || n_heads_q < 1 || kv_dim < 0 || hidden < 0) return false;
+  WsLayout L;
+  const int64_t qt_max = ceil_div64(max_seqlen, kMinBM);
+  L.cell_cap = 2 * (int64_t)batch * qt_max;
+  L.item_cap = (int64_t)batch * n_heads_q * qt_max;
+  if (L.item_cap > INT32_MAX / 4 || L.cell_cap > INT32_MAX / 4) return false;
+  size_t at = 0;
+  L.counters = at;   at = align256(at + 16 * sizeof(int32_t));
+  L.qt_prefix = at;  at = align256(at + sizeof(int32_t) * ((size_t)batch + 1));
+  L.n_sparse = at;   at = align256(at + sizeof(int32_t) * (size_t)batch);
+  L.cells = at;      at = align256(at + 16 * (size_t)L.cell_cap);
+  L.sorted = at;     at = align256(at + 16 * (size_t)L.cell_cap);
+  L.cell_off = at;   at = align256(at + 4 * (size_t)L.cell_cap);
+  L.items = at;      at = align256(at + 16 * (size_t)L.item_cap);
+  // The router's partial sums overlay the start of the workspace: they are dead once
+  // ea_route returns its bits, and calls sharing a workspace are ordered on one stream.
+  L.router_chunks = router_chunks(batch);
+  L.router_partial = 0;
+  const size_t router_bytes =
+      align256(sizeof(float) * (size_t)batch * L.router_chunks * (size_t)kv_dim);
+  L.total = at > router_bytes ? at : router_bytes;
+  *out = L;
+  return true;
+}
+
+}  // namespace ea
+
+using namespace ea;
+
+extern "C" {
+
+size_t ea_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
+                         int32_t hidden) {
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen, n_heads_q, kv_dim, hidden, &L)) return 0;
+  return L.total;
+}
+
+void ea_tile_config(ea_dtype dt, int32_t head_dim, int32_t* bm, int32_t* bn) {
+  int m = 0, n = 0;
+  if (!tile_shape(dt, head_dim, &m, &n)) m = n = 0;
+  if (bm) *bm = m;
+  if (bn) *bn = n;
+}
+
+const char* ea_status_string(ea_status s) {
+  switch (s) {
+    case EA_OK: return "ok";
+    case EA_ERR_INVALID_ARG: return "invalid argument";
+    case EA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EA_ERR_WORKSPACE: return "workspace too small";
+    case EA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* ea_last_error(void) { return g_last_error.c_str(); }
+
+ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
+                   const int32_t* cu_seqlens, int32_t batch, const float* w1, const float* b1,
+                   int32_t hidden, const float* w2, const float* b2, int32_t n_heads_q,
+                   float* logits_out, uint8_t* route_out, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  g_last_error.clear();
+  if (!key_states || !cu_seqlens || !w1 || !b1 || !w2 || !b2 || !route_out || !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (kdt != EA_BF16 && kdt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || kv_dim < 1 || hidden < 1 || n_heads_q < 1)
+    return fail(EA_ERR_INVALID_ARG, "batch, kv_dim, hidden and n_heads_q must be >= 1");
+  if (((size_t)kv_dim + (size_t)hidden) * sizeof(float) > 64 * 1024)
+    return fail(EA_ERR_UNSUPPORTED, "kv_dim + hidden exceeds the MLP's LDS staging (16384)");
+  if (!aligned16(key_states)) return fail(EA_ERR_INVALID_ARG, "key_states must be 16-byte aligned");
+  WsLayout L;
+  if (!ws_layout(batch, 0, n_heads_q, kv_dim, hidden, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  float* partial = (float*)((char*)workspace + L.router_partial);
+  hipError_t e = launch_route(key_states, kdt == EA_BF16 ? 0 : 1, kv_dim, cu_seqlens, batch, w1,
+                              b1, hidden, w2, b2, n_heads_q, logits_out, route_out, partial,
+                              L.router_chunks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return EA_OK;
+}
+
+ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int32_t batch,
+                            int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
+                            ea_dtype dt, int32_t head_dim, int32_t* worklist_out,
+                            int32_t* n_items_out, int32_t* n_items_host, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!route || !cu_seqlens || !worklist_out || !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (batch < 1 || max_seqlen < 0 || n_heads_q < 1)
+    return fail(EA_ERR_INVALID_ARG, "batch < 1, max_seqlen < 0 or n_heads_q < 1");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  int bm = 0, bn = 0;
+  if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (!tile_shape(dt, head_dim, &bm, &bn))
+    return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (ceil_div64(max_seqlen, bn) + 2 > kPlanMaxBins)
+    return fail(EA_ERR_UNSUPPORTED, "max_seqlen exceeds the planner's cost range");
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  ea_status s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn,
+                             (int4*)worklist_out, n_items_out, L, ws, st);
+  if (s != EA_OK) return s;
+  if (n_items_host) {
+    hipError_t e = hipMemcpyAsync(n_items_host, ws + L.counters, sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "item count copy");
+  }
+  return EA_OK;
+}
+
+ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, void* o,
+                                 ea_dtype dt, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, int32_t batch,
+                                 int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                 int32_t head_dim, const uint8_t* route, int32_t sink,
+                                 int32_t window, float scale, float* lse_out,
+                                 int32_t* worklist_out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  g_last_error.clear();
+  int bm = 0, bn = 0;
+  ea_status s = check_attn_args(q, k, v, o, dt, cu_seqlens, batch, max_seqlen, n_heads_q,
+                                n_heads_kv, head_dim, route, sink, window, scale, workspace,
+                                &bm, &bn);
+  if (s != EA_OK) return s;
+  if (cu_seqlens_host) {
+    s = check_cu_host(cu_seqlens_host, batch, max_seqlen);
+    if (s != EA_OK) return s;
+    const int64_t T = cu_seqlens_host[batch];
+    const size_t elem = dt == EA_BF16 ? 2 : 4;
+    const size_t nq = (size_t)T * n_heads_q * head_dim * elem;
+    const size_t nkv = (size_t)T * n_heads_kv * head_dim * elem;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+      return fail(EA_ERR_INVALID_ARG, "o overlaps q, k or v");
+  }
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  int4* items = worklist_out ? (int4*)worklist_out : (int4*)(ws + L.items);
+  int32_t* counters = (int32_t*)(ws + L.counters);
+  s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn, items,
+                   nullptr, L, ws, st);
+  if (s != EA_OK) return s;
+  return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
+                      sink, window, scale, lse_out, items, counters, counters + 1, 0, st);
+}
+
+ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+                             const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                             int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                             const uint8_t* route, int32_t sink, int32_t window, float scale,
+                             float* lse_out, const int32_t* worklist, const int32_t* n_items,
+                             int32_t grid_blocks, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  g_last_error.clear();
+  int bm = 0, bn = 0;
+  ea_status s = check_attn_args(q, k, v, o, dt, cu_seqlens, batch, max_seqlen, n_heads_q,
+                                n_heads_kv, head_dim, route, sink, window, scale, workspace,
+                                &bm, &bn);
+  if (s != EA_OK) return s;
+  if (!worklist || !n_items) return fail(EA_ERR_INVALID_ARG, "null work list or item count");
+  if (grid_blocks < 0) return fail(EA_ERR_INVALID_ARG, "grid_blocks < 0");
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  char* ws = (char*)workspace;
+  int32_t* counters = (int32_t*)(ws + L.counters);
+  return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
+                      sink, window, scale, lse_out, (const int4*)worklist, n_items, counters + 1,
+                      grid_blocks, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// ea_internal.h -- shared declarations of libea's host layer and its HIP kernels.
+// Not installed; the public ABI is include/ea.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ea {
+
+// ---------------------------------------------------------------- tile shapes
+// bf16 path: 4 wavefronts x 32 query rows = 128-row q-tiles, 64-key tiles.
+// fp32 path: 64-row q-tiles, 32-key tiles.
+constexpr int kBf16BM = 128;
+constexpr int kBf16BN = 64;
+constexpr int kF32BM = 64;
+constexpr int kF32BN = 32;
+constexpr int kMinBM = 64;          // smallest q-tile over all paths (sizes the work list)
+constexpr int kMinBN = 32;          // smallest key tile (sizes the planner's cost bins)
+constexpr int kPlanMaxBins = 16384; // planner cost histogram lives in LDS
+
+// ---------------------------------------------------------------- workspace
+struct WsLayout {
+  int router_chunks = 0;
+  size_t router_partial = 0;  // float [batch][router_chunks][kv_dim], overlays the rest
+  size_t qt_prefix = 0;       // int32 [batch + 1]
+  size_t n_sparse = 0;        // int32 [batch]
+  size_t cells = 0;           // int4 [2 * batch * qt_max]   (unsorted, slot order)
+  size_t sorted = 0;          // int4 [2 * batch * qt_max]   (cost descending)
+  size_t cell_off = 0;        // int32 [2 * batch * qt_max]  (item offset per sorted cell)
+  size_t items = 0;           // int4 [batch * n_heads_q * qt_max] (internal work list)
+  size_t counters = 0;        // int32 [16]: 0 n_items, 1 queue head
+  size_t total = 0;
+  int64_t cell_cap = 0;
+  int64_t item_cap = 0;
+};
+
+// Returns false if the sizes overflow what the layout can describe.
+bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
+               int32_t hidden, WsLayout* out);
+
+int router_chunks(int32_t batch);
+
+// ---------------------------------------------------------------- launches
+// Each returns the hipError_t of its launch.
+hipError_t launch_route(const void* ks, int kdt, int kv_dim, const int32_t* cu, int batch,
+                        const float* w1, const float* b1, int hidden, const float* w2,
+                        const float* b2, int n_heads_q, float* logits, uint8_t* route,
+                        float* partial, int chunks, hipStream_t stream);
+
+struct PlanArgs {
+  const uint8_t* route;
+  const int32_t* cu;
+  int batch, n_heads_q, sink, window, bm, bn, bins;
+  int32_t* qt_prefix;
+  int32_t* n_sparse;
+  int4* cells;
+  int4* sorted;
+  int32_t* cell_off;
+  int4* items;
+  int32_t* counters;      // [0] n_items, [1] queue head (reset to 0)
+  int32_t* n_items_out;   // nullable
+};
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* cu;
+  const uint8_t* route;
+  const int4* items;
+  const int32_t* n_items;
+  int32_t* queue;
+  float* lse;
+  int batch, n_heads_q, n_heads_kv, head_dim, sink, window;
+  float scale;
+};
+hipError_t launch_reset_queue(int32_t* queue, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnArgs& a, int grid, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, int grid, hipStream_t stream);
+// Workgroups of each attention kernel that fit on one CU at once.
+int attn_bf16_blocks_per_cu();
+int attn_f32_blocks_per_cu();
+
+}  // namespace ea

@@ -1,0 +1,167 @@
+"""Thin ctypes binding of libea.so (include/ea.h).  Argument marshalling only: every step
+of the path runs in the library's HIP kernels.  Tensors are torch tensors on the GPU
+(torch supplies device memory and the current stream); the functions keep the C names
+without the ``ea_`` prefix.  A non-OK status raises :class:`EAError`.
+
+The library must have been built (``python -m full_attention_long_amd.build``); if it is
+missing, loading raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libea.so")
+
+EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_HIP = range(5)
+EA_BF16, EA_F32 = 0, 1
+
+EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_error",
+           "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run")
+
+_lib = None
+
+
+class EAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_string(status)} ({status}): {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def lib():
+    """Load libea.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise OSError(f"{LIB_PATH} not found: build it with python -m full_attention_long_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    L.ea_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.ea_workspace_size.restype = sz
+    L.ea_tile_config.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.ea_tile_config.restype = None
+    L.ea_status_string.argtypes = [i32]
+    L.ea_status_string.restype = ctypes.c_char_p
+    L.ea_last_error.argtypes = []
+    L.ea_last_error.restype = ctypes.c_char_p
+    L.ea_route.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P, sz, P]
+    L.ea_route.restype = i32
+    L.ea_build_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
+    L.ea_build_worklist.restype = i32
+    L.ea_hybrid_attn_prefill.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P,
+                                         i32, i32, f32, P, P, P, sz, P]
+    L.ea_hybrid_attn_prefill.restype = i32
+    L.ea_hybrid_attn_run.argtypes = [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
+                                     f32, P, P, P, i32, P, sz, P]
+    L.ea_hybrid_attn_run.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(s: int) -> str:
+    return lib().ea_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib().ea_last_error().decode()
+
+
+def _check(status: int):
+    if status != EA_OK:
+        raise EAError(status, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return EA_BF16
+    if dtype == torch.float32:
+        return EA_F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def workspace_size(batch, max_seqlen, n_heads_q, kv_dim=0, hidden=0) -> int:
+    return int(lib().ea_workspace_size(batch, max_seqlen, n_heads_q, kv_dim, hidden))
+
+
+def tile_config(dt: int, head_dim: int):
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    lib().ea_tile_config(int(dt), int(head_dim), ctypes.byref(bm), ctypes.byref(bn))
+    return bm.value, bn.value
+
+
+def route(key_states, cu_seqlens, w1, b1, w2, b2, route_out, workspace, logits_out=None,
+          stream=None):
+    """ea_route: key_states [T, C] (bf16/fp32), w1 [H, C], b1 [H], w2 [Hq, H], b2 [Hq] fp32;
+    writes route_out [B, Hq] uint8 and optionally logits_out [B, Hq] fp32."""
+    batch = cu_seqlens.numel() - 1
+    _check(lib().ea_route(_ptr(key_states), dtype_code(key_states.dtype), key_states.shape[-1],
+                          _ptr(cu_seqlens), batch, _ptr(w1), _ptr(b1), w1.shape[0],
+                          _ptr(w2), _ptr(b2), w2.shape[0], _ptr(logits_out), _ptr(route_out),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream)))
+
+
+def build_worklist(route_bits, cu_seqlens, max_seqlen, n_heads_q, sink, window, dt, head_dim,
+                   worklist_out, workspace, n_items_out=None, want_count=True, stream=None):
+    """ea_build_worklist; returns the item count when want_count (synchronises)."""
+    batch = cu_seqlens.numel() - 1
+    n_host = ctypes.c_int32(-1)
+    _check(lib().ea_build_worklist(_ptr(route_bits), _ptr(cu_seqlens), batch, max_seqlen,
+                                   n_heads_q, sink, window, int(dt), head_dim,
+                                   _ptr(worklist_out), _ptr(n_items_out),
+                                   ctypes.byref(n_host) if want_count else None,
+                                   _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+    return n_host.value if want_count else None
+
+
+def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window,
+                        workspace, scale=0.0, cu_seqlens_host=None, lse_out=None,
+                        worklist_out=None, stream=None):
+    """ea_hybrid_attn_prefill: q/o [T, Hq, D], k/v [T, Hkv, D] (bf16 or fp32)."""
+    batch = cu_seqlens.numel() - 1
+    host = None
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu_seqlens_host])
+    _check(lib().ea_hybrid_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype),
+                                        _ptr(cu_seqlens), host, batch, max_seqlen,
+                                        q.shape[1], k.shape[1], q.shape[2], _ptr(route_bits),
+                                        sink, window, float(scale), _ptr(lse_out),
+                                        _ptr(worklist_out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
+
+
+def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window, worklist,
+                    n_items, workspace, scale=0.0, lse_out=None, grid_blocks=0, stream=None):
+    """ea_hybrid_attn_run on a work list from build_worklist (n_items: device int32)."""
+    batch = cu_seqlens.numel() - 1
+    _check(lib().ea_hybrid_attn_run(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype),
+                                    _ptr(cu_seqlens), batch, max_seqlen, q.shape[1], k.shape[1],
+                                    q.shape[2], _ptr(route_bits), sink, window, float(scale),
+                                    _ptr(lse_out), _ptr(worklist), _ptr(n_items),
+                                    int(grid_blocks), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))

@@ -1,0 +1,167 @@
+/*
+ * ea.h -- C ABI of libea.so: routed hybrid-attention prefill (Elastic Attention) on AMD
+ * MI355X (gfx950).
+ *
+ * The method (web pages on "Elastic Attention: Test-time Adaptive Sparsity Ratios for
+ * Efficient Transformers", arXiv:2601.17367):
+ *   - Elastic Attention blog post, section 2.1 "Attention Router": a light router reads
+ *     the current key hidden states and an MLP emits one routing signal r per head;
+ *     r = 0 runs Full Attention, r = 1 runs Sparse Attention; the per-mode outputs are
+ *     concatenated.
+ *   - same post, section 1: hybrid schemes let some heads attend globally and others only
+ *     to a local or sliding window; gist.science explanation, section "问题所在": sparse
+ *     reading looks at the first and the last pages only.  This library fixes the sparse
+ *     pattern as an attention sink (the first `sink` keys of each sequence) united with a
+ *     causal sliding window of `window` keys that ends at the query (diagonal included).
+ *   - same post, section 3 "Fused Kernel": the routing decision is handed to a single
+ *     kernel as metadata and one launch serves full and sparse heads together.
+ *
+ * Conventions shared by every entry point
+ *   Pointers are DEVICE pointers unless their name ends in _host.  `stream` is a
+ *   hipStream_t passed as void* (NULL = the null stream).  Work is enqueued
+ *   asynchronously on `stream`; no entry point synchronises the host unless it writes a
+ *   *_host output.
+ *   Layout is packed token-major ("THD"): sequence b owns tokens
+ *   [cu_seqlens[b], cu_seqlens[b+1]) and positions restart at 0 in every sequence;
+ *   no token attends across a sequence boundary.  Q and O are [T, n_heads_q, head_dim],
+ *   K and V are [T, n_heads_kv, head_dim], contiguous, 16-byte aligned.  Query head h
+ *   reads KV head h / (n_heads_q / n_heads_kv).  The output of head h for token t is
+ *   written to O[t, h, :], so O viewed as [T, n_heads_q * head_dim] is the concatenation
+ *   of the heads.
+ *   The caller owns every buffer.  The library allocates no device memory; all scratch
+ *   lives in the caller's `workspace` (size from ea_workspace_size).  Calls that share a
+ *   workspace must be ordered on one stream.
+ *   Errors: every argument check runs on the host before anything is enqueued; on an
+ *   error nothing is launched and no output is touched.  HIP failures return
+ *   EA_ERR_HIP.  ea_last_error() gives a detail string for the calling thread.
+ */
+#ifndef EA_H
+#define EA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EA_OK = 0,
+  EA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned buffer, bad cu_seqlens */
+  EA_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement            */
+  EA_ERR_WORKSPACE = 3,   /* workspace smaller than ea_workspace_size() demands       */
+  EA_ERR_HIP = 4          /* a HIP runtime call failed (detail in ea_last_error())    */
+} ea_status;
+
+typedef enum { EA_BF16 = 0, EA_F32 = 1 } ea_dtype;
+
+/*
+ * Bytes of workspace that suffice for every entry point below called with these sizes
+ * (any dtype, any head_dim).  batch >= 1, max_seqlen >= 0, n_heads_q >= 1; kv_dim and
+ * hidden are the router's input and hidden widths (0 if ea_route is not used).
+ * Returns 0 if the sizes are invalid.
+ */
+size_t ea_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
+                         int32_t hidden);
+
+/*
+ * Tile shape of the attention kernel for (dt, head_dim): *bm query rows per work item
+ * and *bn keys per key tile.  These fix the work-list items and their costs.
+ * Unsupported combinations set both to 0.
+ */
+void ea_tile_config(ea_dtype dt, int32_t head_dim, int32_t* bm, int32_t* bn);
+
+/* Static text for a status code; never NULL. */
+const char* ea_status_string(ea_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* ea_last_error(void);
+
+/*
+ * Attention Router (blog post section 2.1; 0.27M parameters per layer for an 8B model,
+ * section 2.2).  For every sequence b:
+ *   x_b = mean over the sequence's tokens of key_states[t, :]   (zero vector if empty)
+ *   z_b = W2 * SiLU(W1 * x_b + b1) + b2,   SiLU(u) = u / (1 + exp(-u))
+ *   route_out[b, h] = (z_b[h] > 0) ? 1 : 0    (1 = sparse, 0 = full; z == 0 is full)
+ * key_states  [T, kv_dim], dtype kdt (EA_BF16 or EA_F32); a layer's K viewed as
+ *             [T, n_heads_kv * head_dim] is a valid input
+ * cu_seqlens  [batch + 1] int32, device
+ * w1 [hidden, kv_dim], b1 [hidden], w2 [n_heads_q, hidden], b2 [n_heads_q]: fp32, row-major
+ * logits_out  [batch, n_heads_q] fp32 (nullable), route_out [batch, n_heads_q] uint8
+ * The mean is accumulated in fp32 in a fixed order (deterministic); the MLP runs in fp32.
+ */
+ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
+                   const int32_t* cu_seqlens, int32_t batch,
+                   const float* w1, const float* b1, int32_t hidden,
+                   const float* w2, const float* b2, int32_t n_heads_q,
+                   float* logits_out, uint8_t* route_out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Work list of the fused launch (blog post section 3: routing reaches the kernel as
+ * metadata).  One item per (sequence b, query head h, q-tile j of bm rows), as four
+ * int32 {b, h, j, cost}, where cost is the number of bn-key tiles that hold at least one
+ * visible (query, key) pair for the item's rows: tiles 0..(m1-1)/bn for a full head,
+ * the sink tiles united with the window tiles for a sparse head (rows [m0, m1)).
+ * Order: cost descending, ties by (b, j, h) ascending -- longest first, so long full-head
+ * items start early and short sparse items fill the tail; sibling heads of one q-tile
+ * are adjacent.  The order is unique, so the list is reproducible bit for bit.
+ * worklist_out  [capacity, 4] int32 with capacity >= batch * n_heads_q * ceil(max_seqlen/bm)
+ * n_items_out   device int32 (nullable): item count.  n_items_host (nullable): if given,
+ *               the call synchronises `stream` and stores the count there.
+ * dt, head_dim select (bm, bn) as ea_tile_config.  max_seqlen bounds every sequence.
+ */
+ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int32_t batch,
+                            int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
+                            ea_dtype dt, int32_t head_dim,
+                            int32_t* worklist_out, int32_t* n_items_out, int32_t* n_items_host,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Routed hybrid-attention prefill in one persistent launch (blog post sections 2.1 and 3).
+ * For sequence b, head h, position i (0-based in the sequence), with g the KV head of h:
+ *   visible(i) = { j : j <= i }                                     if route[b, h] == 0
+ *              = { j : j <= i and (j < sink or j > i - window) }     otherwise
+ *   o = sum_{j in visible} softmax_j(scale * <q_i, k_j>) v_j   -> O[cu_seqlens[b] + i, h, :]
+ *   lse = log sum_{j in visible} exp(scale * <q_i, k_j>)        -> lse_out[h, cu_seqlens[b] + i]
+ * q, k, v, o   dtype dt: EA_BF16 (bf16 MFMA, fp32 accumulation and softmax, P rounded to
+ *              bf16 for P*V, O rounded to nearest even) or EA_F32 (fp32 throughout)
+ * cu_seqlens       [batch + 1] int32 device; cu_seqlens_host: nullable host copy that
+ *                  enables the host-side checks (monotone, starts at 0, lengths <=
+ *                  max_seqlen) and the exact aliasing check of o against q, k, v
+ * head_dim 64 or 128; n_heads_q % n_heads_kv == 0; sink >= 0; window >= 1;
+ * scale <= 0 selects 1/sqrt(head_dim)
+ * route        [batch, n_heads_q] uint8 (0 full, nonzero sparse)
+ * lse_out      nullable, [n_heads_q, T] fp32
+ * worklist_out nullable, receives the work list (see ea_build_worklist) for inspection
+ * o must not overlap q, k or v.  Results do not depend on scheduling: every output
+ * element is written by exactly one work item.
+ */
+ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, void* o,
+                                 ea_dtype dt, const int32_t* cu_seqlens,
+                                 const int32_t* cu_seqlens_host, int32_t batch,
+                                 int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                 int32_t head_dim, const uint8_t* route, int32_t sink,
+                                 int32_t window, float scale, float* lse_out,
+                                 int32_t* worklist_out, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * The attention half of ea_hybrid_attn_prefill on a work list made by ea_build_worklist
+ * (same dt, head_dim, sink, window, route and cu_seqlens).  worklist and n_items are
+ * device pointers.  grid_blocks sets the number of persistent workgroups (0 = one per
+ * resident slot on the device); the output does not depend on it.
+ */
+ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+                             const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                             int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
+                             const uint8_t* route, int32_t sink, int32_t window, float scale,
+                             float* lse_out, const int32_t* worklist, const int32_t* n_items,
+                             int32_t grid_blocks, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EA_H */

@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every entry point
+declared in include/ea.h, reports its tile shapes and workspace sizes, and rejects bad
+arguments on the host with the documented status before any HIP call (so fake, never
+dereferenced pointers are safe here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from full_attention_long_amd import ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ea.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ea_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    L = ea.lib()
+    names = header_functions()
+    assert set(names) == set(ea.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_tile_config_and_workspace():
+    assert ea.tile_config(ea.EA_BF16, 128) == (128, 64)
+    assert ea.tile_config(ea.EA_BF16, 64) == (128, 64)
+    assert ea.tile_config(ea.EA_F32, 64) == (64, 32)
+    assert ea.tile_config(ea.EA_F32, 96) == (0, 0)
+    assert ea.tile_config(7, 128) == (0, 0)
+    a = ea.workspace_size(1, 32768, 32)
+    b = ea.workspace_size(1, 32768, 32, 1024, 256)
+    c = ea.workspace_size(4, 32768, 32)
+    assert 0 < a <= b and a < c
+    assert ea.workspace_size(0, 10, 1) == 0 and ea.workspace_size(1, -1, 1) == 0
+    for s in range(5):
+        assert ea.status_string(s)
+    assert ea.status_string(99) == "unknown status"
+
+
+def prefill(**kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, dt=ea.EA_BF16,
+                cu=FAKE, cu_host=None, batch=1, max_seqlen=128, hq=4, hkv=2, d=128,
+                route=FAKE, sink=4, window=16, scale=0.0, lse=None, wl=None, ws=FAKE,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return ea.lib().ea_hybrid_attn_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.EA_ERR_INVALID_ARG),
+    (dict(ws=None), ea.EA_ERR_INVALID_ARG),
+    (dict(route=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dt=5), ea.EA_ERR_INVALID_ARG),
+    (dict(batch=0), ea.EA_ERR_INVALID_ARG),
+    (dict(max_seqlen=-1), ea.EA_ERR_INVALID_ARG),
+    (dict(hq=6, hkv=4), ea.EA_ERR_INVALID_ARG),
+    (dict(hkv=0), ea.EA_ERR_INVALID_ARG),
+    (dict(window=0), ea.EA_ERR_INVALID_ARG),
+    (dict(sink=-1), ea.EA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ea.EA_ERR_INVALID_ARG),
+    (dict(d=96), ea.EA_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), ea.EA_ERR_INVALID_ARG),
+    (dict(o=FAKE), ea.EA_ERR_INVALID_ARG),
+    (dict(max_seqlen=1 << 24), ea.EA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16), ea.EA_ERR_WORKSPACE),
+])
+def test_prefill_rejects(kw, status):
+    assert prefill(**kw) == status
+    assert ea.last_error()
+
+
+def test_prefill_host_cu_checks():
+    bad = [(0, 200), (5, 10), (0, 10, 5)]
+    for cu in bad:
+        n = len(cu) - 1
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        assert prefill(cu_host=arr, batch=n) == ea.EA_ERR_INVALID_ARG
+    # o overlapping k inside its extent
+    arr = (ctypes.c_int32 * 2)(0, 100)
+    assert prefill(cu_host=arr, o=FAKE + 0x1000 + 0x10) == ea.EA_ERR_INVALID_ARG
+
+
+def test_route_and_worklist_reject():
+    L = ea.lib()
+    ok = dict(ks=FAKE, kdt=ea.EA_BF16, kv=1024, cu=FAKE, batch=1, w1=FAKE, b1=FAKE, hid=256,
+              w2=FAKE, b2=FAKE, hq=32, logits=None, r=FAKE, ws=FAKE, wsb=1 << 30, st=None)
+    for kw, st in [(dict(ks=None), 1), (dict(r=None), 1), (dict(kv=0), 1), (dict(kdt=3), 1),
+                   (dict(kv=16384, hid=256), 2), (dict(ks=FAKE + 4), 1), (dict(wsb=0), 3)]:
+        a = dict(ok)
+        a.update(kw)
+        assert L.ea_route(*a.values()) == st, kw
+    okw = dict(r=FAKE, cu=FAKE, batch=1, maxlen=100, hq=4, sink=0, win=1, dt=0, d=128, wl=FAKE,
+               nout=None, nhost=None, ws=FAKE, wsb=1 << 30, st=None)
+    for kw, st in [(dict(wl=None), 1), (dict(win=0), 1), (dict(d=80), 2), (dict(dt=9), 1),
+                   (dict(wsb=8), 3), (dict(maxlen=1 << 26), 2)]:
+        a = dict(okw)
+        a.update(kw)
+        assert L.ea_build_worklist(*a.values()) == st, kw
+
+
+def test_run_rejects():
+    L = ea.lib()
+    base = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 0, FAKE, 1, 128, 4, 2, 128,
+            FAKE, 0, 16, 0.0, None, FAKE, FAKE, 0, FAKE, 1 << 30, None]
+    a = list(base)
+    a[16] = None  # work list
+    assert L.ea_hybrid_attn_run(*a) == ea.EA_ERR_INVALID_ARG
+    a = list(base)
+    a[18] = -1    # grid_blocks
+    assert L.ea_hybrid_attn_run(*a) == ea.EA_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful without a GPU")
+def test_valid_call_without_gpu_reports_hip_error():
+    # every check passes, so the first HIP call runs and fails: the status is EA_ERR_HIP
+    assert prefill() == ea.EA_ERR_HIP
+    assert "device" in ea.last_error() or "launch" in ea.last_error()
