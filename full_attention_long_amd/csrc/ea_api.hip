@@ -67,6 +67,15 @@ hipError_t cu_count(int* out) {
   return hipSuccess;
 }
 
+// The planner holds its state in one workgroup's LDS: bound the cells, sequences, heads.
+ea_status check_plan_limits(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int bm) {
+  if (batch > kPlanMaxBatch) return fail(EA_ERR_UNSUPPORTED, "more than 1024 sequences");
+  if (n_heads_q > kPlanMaxHeads) return fail(EA_ERR_UNSUPPORTED, "more than 128 query heads");
+  if (2 * (int64_t)batch * ceil_div64(max_seqlen, bm) > kPlanMaxCells)
+    return fail(EA_ERR_UNSUPPORTED, "batch * ceil(max_seqlen / bm) exceeds 4096 q-tiles");
+  return EA_OK;
+}
+
 // Checks shared by the attention entry points.  Fills bm/bn.
 ea_status check_attn_args(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
                           const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
@@ -91,9 +100,7 @@ ea_status check_attn_args(const void* q, const void* k, const void* v, void* o, 
   if ((int64_t)max_seqlen * n_heads_kv * head_dim * elem >= ((int64_t)1 << 31) ||
       (int64_t)(*bm + 1) * n_heads_q * head_dim * elem >= ((int64_t)1 << 31))
     return fail(EA_ERR_UNSUPPORTED, "sequence too long for 32-bit per-sequence addressing");
-  if (ceil_div64(max_seqlen, *bn) + 2 > kPlanMaxBins)
-    return fail(EA_ERR_UNSUPPORTED, "max_seqlen exceeds the planner's cost range");
-  return EA_OK;
+  return check_plan_limits(batch, max_seqlen, n_heads_q, *bm);
 }
 
 ea_status check_cu_host(const int32_t* cu, int32_t batch, int32_t max_seqlen) {
@@ -124,12 +131,6 @@ ea_status enqueue_plan(const uint8_t* route, const int32_t* cu, int32_t batch,
   p.window = window;
   p.bm = bm;
   p.bn = bn;
-  p.bins = (int)(ceil_div64(max_seqlen, bn) + 2);
-  p.qt_prefix = (int32_t*)(ws + L.qt_prefix);
-  p.n_sparse = (int32_t*)(ws + L.n_sparse);
-  p.cells = (int4*)(ws + L.cells);
-  p.sorted = (int4*)(ws + L.sorted);
-  p.cell_off = (int32_t*)(ws + L.cell_off);
   p.items = items;
   p.counters = (int32_t*)(ws + L.counters);
   p.n_items_out = n_items_out;
@@ -168,9 +169,7 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
     if (e != hipSuccess) return hip_fail(e, "device query");
     grid = ncu * (dt == EA_BF16 ? attn_bf16_blocks_per_cu() : attn_f32_blocks_per_cu());
   }
-  hipError_t e = launch_reset_queue(queue, stream);
-  if (e != hipSuccess) return hip_fail(e, "queue reset launch");
-  e = dt == EA_BF16 ? launch_attn_bf16(a, grid, stream) : launch_attn_f32(a, grid, stream);
+  hipError_t e = dt == EA_BF16 ? launch_attn_bf16(a, grid, stream) : launch_attn_f32(a, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return EA_OK;
 }
@@ -182,24 +181,22 @@ bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_
   if (batch < 1 || max_seqlen < 0 || n_heads_q < 1 || kv_dim < 0 || hidden < 0) return false;
   WsLayout L;
   const int64_t qt_max = ceil_div64(max_seqlen, kMinBM);
-  L.cell_cap = 2 * (int64_t)batch * qt_max;
   L.item_cap = (int64_t)batch * n_heads_q * qt_max;
-  if (L.item_cap > INT32_MAX / 4 || L.cell_cap > INT32_MAX / 4) return false;
+  if (L.item_cap > INT32_MAX / 4) return false;
   size_t at = 0;
   L.counters = at;   at = align256(at + 16 * sizeof(int32_t));
-  L.qt_prefix = at;  at = align256(at + sizeof(int32_t) * ((size_t)batch + 1));
-  L.n_sparse = at;   at = align256(at + sizeof(int32_t) * (size_t)batch);
-  L.cells = at;      at = align256(at + 16 * (size_t)L.cell_cap);
-  L.sorted = at;     at = align256(at + 16 * (size_t)L.cell_cap);
-  L.cell_off = at;   at = align256(at + 4 * (size_t)L.cell_cap);
   L.items = at;      at = align256(at + 16 * (size_t)L.item_cap);
-  // The router's partial sums overlay the start of the workspace: they are dead once
-  // ea_route returns its bits, and calls sharing a workspace are ordered on one stream.
+  // The router's scratch overlays the start of the workspace: it is dead once ea_route
+  // has written its bits, and calls that share a workspace are ordered on one stream.
   L.router_chunks = router_chunks(batch);
-  L.router_partial = 0;
-  const size_t router_bytes =
-      align256(sizeof(float) * (size_t)batch * L.router_chunks * (size_t)kv_dim);
-  L.total = at > router_bytes ? at : router_bytes;
+  size_t r = 0;
+  L.router_partial = r;
+  r = align256(r + sizeof(float) * (size_t)batch * L.router_chunks * (size_t)kv_dim);
+  L.router_x = r;
+  r = align256(r + sizeof(float) * (size_t)batch * (size_t)kv_dim);
+  L.router_h = r;
+  r = align256(r + sizeof(float) * (size_t)batch * (size_t)hidden);
+  L.total = at > r ? at : r;
   *out = L;
   return true;
 }
@@ -248,17 +245,17 @@ ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
   if (kdt != EA_BF16 && kdt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
   if (batch < 1 || kv_dim < 1 || hidden < 1 || n_heads_q < 1)
     return fail(EA_ERR_INVALID_ARG, "batch, kv_dim, hidden and n_heads_q must be >= 1");
-  if (((size_t)kv_dim + (size_t)hidden) * sizeof(float) > 64 * 1024)
-    return fail(EA_ERR_UNSUPPORTED, "kv_dim + hidden exceeds the MLP's LDS staging (16384)");
   if (!aligned16(key_states)) return fail(EA_ERR_INVALID_ARG, "key_states must be 16-byte aligned");
   WsLayout L;
   if (!ws_layout(batch, 0, n_heads_q, kv_dim, hidden, &L))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
   if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
-  float* partial = (float*)((char*)workspace + L.router_partial);
+  char* ws = (char*)workspace;
   hipError_t e = launch_route(key_states, kdt == EA_BF16 ? 0 : 1, kv_dim, cu_seqlens, batch, w1,
-                              b1, hidden, w2, b2, n_heads_q, logits_out, route_out, partial,
-                              L.router_chunks, (hipStream_t)stream);
+                              b1, hidden, w2, b2, n_heads_q, logits_out, route_out,
+                              (float*)(ws + L.router_partial), L.router_chunks,
+                              (float*)(ws + L.router_x), (float*)(ws + L.router_h),
+                              (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   return EA_OK;
 }
@@ -278,16 +275,16 @@ ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int
   if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
   if (!tile_shape(dt, head_dim, &bm, &bn))
     return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-  if (ceil_div64(max_seqlen, bn) + 2 > kPlanMaxBins)
-    return fail(EA_ERR_UNSUPPORTED, "max_seqlen exceeds the planner's cost range");
+  ea_status s = check_plan_limits(batch, max_seqlen, n_heads_q, bm);
+  if (s != EA_OK) return s;
   WsLayout L;
   if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
   if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
-  ea_status s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn,
-                             (int4*)worklist_out, n_items_out, L, ws, st);
+  s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn,
+                   (int4*)worklist_out, n_items_out, L, ws, st);
   if (s != EA_OK) return s;
   if (n_items_host) {
     hipError_t e = hipMemcpyAsync(n_items_host, ws + L.counters, sizeof(int32_t),

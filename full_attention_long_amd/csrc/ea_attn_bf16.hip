@@ -22,11 +22,17 @@
 //     row-major V tile, and the contraction order of keys is permuted consistently on
 //     both operands to match the accumulator layout.
 //   * K and V tiles are double buffered in LDS (global loads for tile n+1 are in flight
-//     while tile n is computed) with padded rows: K rows stride 272 B and V rows 288 B,
-//     which keep the b128 K reads and the transposing V reads free of bank conflicts.
-//   * Softmax uses exp2 with log2(e) folded into the scale; all state is fp32.
+//     while tile n is computed) with padded rows: K rows stride 272 B and V rows 320 B
+//     (D = 128), which keep the b128 K reads and the transposing V reads free of bank
+//     conflicts on the 64-bank LDS.
+//   * Softmax uses exp2 with log2(e) folded into the scale; all state is fp32.  Lazy
+//     rescaling: the running max used in the exponent only moves when a row's max grows
+//     by more than 2^8 in exp2 units (or on the first visible tile), so most tiles skip
+//     the O *= alpha pass; P stays below 256, well inside bf16 and fp32 range.
 //   * Raw buffer loads/stores bound every access: keys past the sequence end read as
 //     zero and rows past the tile end are not stored.
+#include <climits>
+
 #include "ea_device.h"
 #include "ea_internal.h"
 
@@ -43,7 +49,7 @@ constexpr int kSubN = BN / 32;   // 32-key MFMA sub-tiles per key tile
 template <int D>
 struct Shape {
   static constexpr int KS = D + 8;     // K row stride in LDS (elements)
-  static constexpr int VS = D + 16;    // V row stride in LDS (elements)
+  static constexpr int VS = D + 32;    // V row stride in LDS (elements)
   static constexpr int KTILE = BN * KS;
   static constexpr int VTILE = BN * VS;
   static constexpr int LDS_BYTES = 2 * (KTILE + VTILE) * 2;
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int crow = tid / S::CHUNKS, cch = tid % S::CHUNKS;
 
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(a.queue, 1);
+    if (tid == 0) s_item = atomicAdd(&a.queue[0], 1);
     __syncthreads();
     const int it = s_item;
     if (it >= n_items) break;
@@ -193,14 +199,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
 
       if (tile_needs_mask(kt, sparse, m0, m1, a.sink, a.window)) {
+        // key kj = kt*BN + off is visible to query qi iff off <= qi - kbase and, for a
+        // sparse head, (off >= qi - window + 1 - kbase or off < sink - kbase); branch-free
+        const int kbase = kt * BN;
+        const int lim = qi - kbase;
+        const int wlo = sparse ? qi - a.window + 1 - kbase : INT_MIN;
+        const int slim = sparse ? a.sink - kbase : INT_MIN;
 #pragma unroll
         for (int j = 0; j < kSubN; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kj = kt * BN + 32 * j + 8 * (r / 4) + 4 * g + (r % 4);
-            const bool visible =
-                kj <= qi && (!sparse || kj < a.sink || kj > qi - a.window);
-            if (!visible) sacc[j][r] = -INFINITY;
+            const int off = 32 * j + 8 * (r / 4) + 4 * g + (r % 4);
+            const bool visible = (off <= lim) & ((off >= wlo) | (off < slim));
+            sacc[j][r] = visible ? sacc[j][r] : -INFINITY;
           }
       }
 
@@ -211,10 +222,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[j][r]);
       mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float mc = m_use * c_log2;
-      const float alpha = __builtin_amdgcn_exp2f(m_run * c_log2 - mc);
+      // rescale only when some row of the wavefront has a new max (alpha = 1 elsewhere);
+      // P is always relative to the true running max, so its largest entry is exactly 1
+      if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha =
+            m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = (m_run == -INFINITY ? 0.f : m_run) * c_log2;
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < kSubN; ++j)
@@ -224,12 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           sacc[j][r] = p;
           psum += p;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      l_run += psum;
 
       // ---- O^T += V^T P^T over 16-key slices (j, kh): P keys 32j+16kh+8(e/4)+4g+e%4
       const __bf16* vb = vbase + buf * S::VTILE;
@@ -279,6 +295,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       a.lse[(int64_t)h * total_tokens + seq0 + qi] = m_use * a.scale + logf(l_tot);
     }
     __syncthreads();  // s_item and the LDS tiles are reused by the next item
+  }
+  // The last workgroup out leaves the queue counters at zero for the next launch.
+  if (tid == 0 && atomicAdd(&a.queue[1], 1) == (int)gridDim.x - 1) {
+    atomicExch(&a.queue[0], 0);
+    atomicExch(&a.queue[1], 0);
   }
 }
 

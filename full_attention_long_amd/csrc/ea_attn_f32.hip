@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const int total_tokens = a.cu[a.batch];
 
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(a.queue, 1);
+    if (tid == 0) s_item = atomicAdd(&a.queue[0], 1);
     __syncthreads();
     const int it = s_item;
     if (it >= n_items) break;
@@ -137,6 +137,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+  }
+  // The last workgroup out leaves the queue counters at zero for the next launch.
+  if (tid == 0 && atomicAdd(&a.queue[1], 1) == (int)gridDim.x - 1) {
+    atomicExch(&a.queue[0], 0);
+    atomicExch(&a.queue[1], 0);
   }
 }
 

@@ -15,23 +15,22 @@ constexpr int kBf16BM = 128;
 constexpr int kBf16BN = 64;
 constexpr int kF32BM = 64;
 constexpr int kF32BN = 32;
-constexpr int kMinBM = 64;          // smallest q-tile over all paths (sizes the work list)
-constexpr int kMinBN = 32;          // smallest key tile (sizes the planner's cost bins)
-constexpr int kPlanMaxBins = 16384; // planner cost histogram lives in LDS
+constexpr int kMinBM = 64;           // smallest q-tile over all paths (sizes the work list)
+// The planner keeps its whole state in the LDS of one workgroup:
+constexpr int kPlanMaxCells = 8192;  // 2 cells per (sequence, q-tile)
+constexpr int kPlanMaxBatch = 1024;  // sequences per call
+constexpr int kPlanMaxHeads = 128;   // query heads
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
+  // the router's scratch overlays the start of the workspace (see ws_layout)
   int router_chunks = 0;
-  size_t router_partial = 0;  // float [batch][router_chunks][kv_dim], overlays the rest
-  size_t qt_prefix = 0;       // int32 [batch + 1]
-  size_t n_sparse = 0;        // int32 [batch]
-  size_t cells = 0;           // int4 [2 * batch * qt_max]   (unsorted, slot order)
-  size_t sorted = 0;          // int4 [2 * batch * qt_max]   (cost descending)
-  size_t cell_off = 0;        // int32 [2 * batch * qt_max]  (item offset per sorted cell)
+  size_t router_partial = 0;  // float [batch][router_chunks][kv_dim]
+  size_t router_x = 0;        // float [batch][kv_dim]   pooled key states
+  size_t router_h = 0;        // float [batch][hidden]   SiLU(W1 x + b1)
   size_t items = 0;           // int4 [batch * n_heads_q * qt_max] (internal work list)
-  size_t counters = 0;        // int32 [16]: 0 n_items, 1 queue head
+  size_t counters = 0;        // int32 [16]: 0 n_items, 1 queue head, 2 workgroups done
   size_t total = 0;
-  int64_t cell_cap = 0;
   int64_t item_cap = 0;
 };
 
@@ -46,19 +45,14 @@ int router_chunks(int32_t batch);
 hipError_t launch_route(const void* ks, int kdt, int kv_dim, const int32_t* cu, int batch,
                         const float* w1, const float* b1, int hidden, const float* w2,
                         const float* b2, int n_heads_q, float* logits, uint8_t* route,
-                        float* partial, int chunks, hipStream_t stream);
+                        float* partial, int chunks, float* x, float* hv, hipStream_t stream);
 
 struct PlanArgs {
   const uint8_t* route;
   const int32_t* cu;
-  int batch, n_heads_q, sink, window, bm, bn, bins;
-  int32_t* qt_prefix;
-  int32_t* n_sparse;
-  int4* cells;
-  int4* sorted;
-  int32_t* cell_off;
+  int batch, n_heads_q, sink, window, bm, bn;
   int4* items;
-  int32_t* counters;      // [0] n_items, [1] queue head (reset to 0)
+  int32_t* counters;      // [0] n_items, [1] queue head, [2] workgroups done (both zeroed)
   int32_t* n_items_out;   // nullable
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
@@ -72,12 +66,12 @@ struct AttnArgs {
   const uint8_t* route;
   const int4* items;
   const int32_t* n_items;
-  int32_t* queue;
+  int32_t* queue;         // [0] queue head, [1] workgroups done; zero on entry, re-zeroed
+                          // by the last workgroup to finish
   float* lse;
   int batch, n_heads_q, n_heads_kv, head_dim, sink, window;
   float scale;
 };
-hipError_t launch_reset_queue(int32_t* queue, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int grid, hipStream_t stream);
 // Workgroups of each attention kernel that fit on one CU at once.

@@ -8,10 +8,13 @@
 //   sparse head: sink tiles 0 .. ceil(min(sink, m1)/bn)-1 united with window tiles
 //                max(0, m0-window+1)/bn .. (m1-1)/bn
 // Both costs depend on (sequence, q-tile, mode) only, so the planner sorts "cells" -- one
-// per (sequence, q-tile, cost) holding the heads of that cost in ascending order -- and
-// expands them.  Cells are generated in (sequence, q-tile) order and sorted by cost with a
-// stable counting sort, which yields exactly the order cost desc, (sequence, q-tile, head)
-// asc.  Everything runs in one workgroup of 1024 threads; integer only, deterministic.
+// per (sequence, q-tile, cost), holding the heads of that cost -- and expands them.
+// Cell i = 2*slot + sub, slots numbered in (sequence, q-tile) order.  Sorting the keys
+// (cost descending, then i) with a bitonic network in LDS gives exactly the order cost
+// desc, (sequence, q-tile) asc; heads inside a cell are written in ascending order, so
+// the list is cost desc, (sequence, q-tile, head) asc.  One workgroup of 1024 threads,
+// integer only, deterministic.  The planner also zeroes the attention kernel's queue
+// counters.
 #include "ea_device.h"
 #include "ea_internal.h"
 
@@ -20,27 +23,46 @@ namespace ea {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kNumWaves = kPlanThreads / 64;
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-struct Costs {
-  int full, sparse;
+struct HeadMask {
+  uint64_t lo, hi;  // bit h (h < 64 in lo, 64 <= h < 128 in hi) = head h is sparse
 };
 
-__device__ __forceinline__ Costs tile_costs(int len, int qt, int bm, int bn, int sink,
-                                            int window) {
-  const int m0 = qt * bm, m1 = min(m0 + bm, len);
-  const int t_hi = (m1 - 1) / bn;
-  const int n_sink = ceil_div(min(sink, m1), bn);
-  const int t_lo = max(0, m0 - window + 1) / bn;
-  Costs c;
-  c.full = t_hi + 1;
-  c.sparse = n_sink >= t_lo ? t_hi + 1 : n_sink + (t_hi - t_lo + 1);
+// Cell i: {seq, q_tile, cost, mode mask (1 = full heads, 2 = sparse heads)}; cost 0 = empty.
+__device__ __forceinline__ int4 make_cell(int i, const PlanArgs& a, const int* qt_prefix,
+                                          const int* n_sparse_of) {
+  const int f = i >> 1, sub = i & 1;
+  int lo = 0, hi = a.batch - 1;  // last b with qt_prefix[b] <= f (never an empty sequence)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qt_prefix[mid] <= f) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo, qt = f - qt_prefix[b];
+  const int len = a.cu[b + 1] - a.cu[b];
+  const int m0 = qt * a.bm, m1 = min(m0 + a.bm, len);
+  const int t_hi = (m1 - 1) / a.bn;
+  const int n_sink = ceil_div(min(a.sink, m1), a.bn);
+  const int t_lo = max(0, m0 - a.window + 1) / a.bn;
+  const int c_full = t_hi + 1;
+  const int c_sparse = n_sink >= t_lo ? t_hi + 1 : n_sink + (t_hi - t_lo + 1);
+  const int ns = n_sparse_of[b], nf = a.n_heads_q - ns;
+  int4 c = {b, qt, 0, 0};
+  if (nf > 0 && ns > 0 && c_full == c_sparse) {
+    if (sub == 0) { c.z = c_full; c.w = 3; }
+  } else if (nf > 0 && ns > 0) {
+    if (sub == 0) { c.z = c_full; c.w = 1; } else { c.z = c_sparse; c.w = 2; }
+  } else if (sub == 0) {
+    c.z = nf > 0 ? c_full : c_sparse;
+    c.w = nf > 0 ? 1 : 2;
+  }
   return c;
 }
 
-// Block-wide exclusive scan of one int per thread; returns the prefix and the total.
-__device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 32 ints */) {
+// Block-wide exclusive scan of one int per thread; *total receives the sum.
+__device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= kNumWaves+1 */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -52,180 +74,141 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= 32 int
   __syncthreads();
   if (threadIdx.x == 0) {
     int run = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
+    for (int w = 0; w < kNumWaves; ++w) {
       const int t = scratch[w];
       scratch[w] = run;
       run += t;
     }
-    scratch[kPlanThreads / 64] = run;
+    scratch[kNumWaves] = run;
   }
   __syncthreads();
   const int excl = scratch[wave] + incl - v;
-  *total = scratch[kPlanThreads / 64];
+  *total = scratch[kNumWaves];
   __syncthreads();
   return excl;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int bins[kPlanMaxBins];   // histogram, then running start offset per cost
-  __shared__ int scratch[32];
+  __shared__ uint64_t keys[kPlanMaxCells];    // sort keys, then packed sorted cells
+  __shared__ int cell_off[kPlanMaxCells];      // first item of every sorted cell
+  __shared__ HeadMask masks[kPlanMaxBatch];    // sparse heads of every sequence
+  __shared__ int qt_prefix[kPlanMaxBatch + 1]; // first slot of every sequence
+  __shared__ int n_sparse_of[kPlanMaxBatch];
+  __shared__ int scratch[kNumWaves + 1];
+  __shared__ int s_valid;
   const int tid = threadIdx.x;
   const int B = a.batch, Hq = a.n_heads_q;
 
-  // Phase 1: per-sequence q-tile counts (exclusive prefix) and sparse-head counts.
+  // Phase 1: sparse-head masks (one thread per routing byte), then per-sequence q-tile
+  // counts and their exclusive prefix.
+  if (tid == 0) s_valid = 0;
+  for (int b = tid; b < B; b += kPlanThreads) masks[b] = HeadMask{0ull, 0ull};
+  __syncthreads();
+  for (int x = tid; x < B * Hq; x += kPlanThreads) {
+    if (a.route[x] != 0) {
+      const int b = x / Hq, h = x % Hq;
+      if (h < 64) atomicOr((unsigned long long*)&masks[b].lo, 1ull << h);
+      else atomicOr((unsigned long long*)&masks[b].hi, 1ull << (h - 64));
+    }
+  }
+  __syncthreads();
   int carry = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int b = base + tid;
     int nq = 0;
     if (b < B) {
-      const int len = a.cu[b + 1] - a.cu[b];
-      nq = ceil_div(len, a.bm);
-      int ns = 0;
-      for (int h = 0; h < Hq; ++h) ns += a.route[(int64_t)b * Hq + h] != 0;
-      a.n_sparse[b] = ns;
+      nq = ceil_div(a.cu[b + 1] - a.cu[b], a.bm);
+      n_sparse_of[b] = __popcll(masks[b].lo) + __popcll(masks[b].hi);
     }
     int tot;
     const int ex = block_exclusive_scan(nq, &tot, scratch);
-    if (b < B) a.qt_prefix[b] = carry + ex;
+    if (b < B) qt_prefix[b] = carry + ex;
     carry += tot;
   }
-  if (tid == 0) a.qt_prefix[B] = carry;
-  const int slots = carry;  // (sequence, q-tile) pairs
-  for (int i = tid; i < a.bins; i += kPlanThreads) bins[i] = 0;
-  __threadfence_block();
+  if (tid == 0) qt_prefix[B] = carry;
   __syncthreads();
+  const int n_cells = 2 * carry;
+  int n_pad = 2;
+  while (n_pad < n_cells) n_pad <<= 1;
 
-  // Phase 2: two cell slots per (sequence, q-tile); histogram of cell costs.
-  // cell = {seq, q_tile, cost, mode mask (1 full heads, 2 sparse heads)}; cost 0 = empty.
-  for (int f = tid; f < slots; f += kPlanThreads) {
-    int lo = 0, hi = B - 1;  // last b with qt_prefix[b] <= f
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.qt_prefix[mid] <= f) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo, qt = f - a.qt_prefix[b];
-    const int len = a.cu[b + 1] - a.cu[b];
-    const Costs c = tile_costs(len, qt, a.bm, a.bn, a.sink, a.window);
-    const int ns = a.n_sparse[b], nf = Hq - ns;
-    int4 c0 = {b, qt, 0, 0}, c1 = {b, qt, 0, 0};
-    if (nf > 0) {
-      c0.z = c.full;
-      c0.w = 1 | ((ns > 0 && c.sparse == c.full) ? 2 : 0);
-      if (ns > 0 && c.sparse != c.full) { c1.z = c.sparse; c1.w = 2; }
-    } else {
-      c0.z = c.sparse;
-      c0.w = 2;
-    }
-    a.cells[2 * f] = c0;
-    a.cells[2 * f + 1] = c1;
-    if (c0.z > 0) atomicAdd(&bins[c0.z], 1);
-    if (c1.z > 0) atomicAdd(&bins[c1.z], 1);
-  }
-  __syncthreads();
-
-  // Phase 3: start offset of every cost, costs in descending order (exclusive scan of the
-  // reversed histogram, one contiguous run of bins per thread).
-  {
-    const int per = ceil_div(a.bins, kPlanThreads);
-    const int lo = tid * per, hi = min(a.bins, lo + per);
-    int s = 0;
-    for (int i = lo; i < hi; ++i) s += bins[a.bins - 1 - i];
-    int tot;
-    int run = block_exclusive_scan(s, &tot, scratch);
-    for (int i = lo; i < hi; ++i) {
-      const int cidx = a.bins - 1 - i;
-      const int cnt = bins[cidx];
-      bins[cidx] = run;
-      run += cnt;
-    }
-  }
-  __syncthreads();
-
-  // Phase 4: stable scatter of the cells by cost, one wavefront walking the cells in slot
-  // order 64 at a time.  Lanes with equal cost are ranked through ballots over the cost
-  // bits; the first lane of every group advances that cost's start offset.
-  const int n_cells = 2 * slots;
-  if (tid < 64) {
-    const int lane = tid;
-    int nbits = 1;
-    while ((1 << nbits) < a.bins) ++nbits;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < n_cells; base += 64) {
-      const int idx = base + lane;
-      int4 cell = {0, 0, 0, 0};
-      if (idx < n_cells) cell = a.cells[idx];
-      const bool valid = cell.z > 0;
-      uint64_t eq = __ballot(valid);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = (cell.z >> bit) & 1;
-        const uint64_t m = __ballot(set);
-        eq &= set ? m : ~m;
+  // Phase 2: sort keys.  High word: 0x7fffffff - cost (descending cost); low word: i.
+  for (int i = tid; i < n_pad; i += kPlanThreads) {
+    uint64_t key = ~0ull;
+    if (i < n_cells) {
+      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of);
+      if (c.z > 0) {
+        key = ((uint64_t)(0x7fffffff - c.z) << 32) | (uint32_t)i;
+        atomicAdd(&s_valid, 1);
       }
-      if (valid) {
-        const int rank = __popcll(eq & below);
-        const int start = bins[cell.z];
-        a.sorted[start + rank] = cell;
-        // make every lane read `start` before the group leader moves it
-        __builtin_amdgcn_wave_barrier();
-        if (rank == 0) bins[cell.z] = start + __popcll(eq);
-      }
-      __builtin_amdgcn_wave_barrier();
     }
+    keys[i] = key;
   }
-  __threadfence();
   __syncthreads();
 
-  // Phase 5: item offset of every sorted cell (heads per cell), then expansion.
-  int n_valid = 0;  // number of non-empty cells
-  {
-    int cnt = 0;
-    for (int i = tid; i < n_cells; i += kPlanThreads) cnt += a.cells[i].z > 0;
-    int tot;
-    block_exclusive_scan(cnt, &tot, scratch);
-    n_valid = tot;
+  // Phase 3: bitonic sort, ascending.
+  for (int k = 2; k <= n_pad; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n_pad; i += kPlanThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = keys[i], y = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
-  int item_carry = 0;
+
+  // Phase 4: unpack the sorted cells (in place) and give every cell its first item.
+  const int n_valid = s_valid;
+  int items_total = 0;
   for (int base = 0; base < n_valid; base += kPlanThreads) {
-    const int i = base + tid;
+    const int p = base + tid;
     int sz = 0;
-    if (i < n_valid) {
-      const int4 cell = a.sorted[i];
-      const int ns = a.n_sparse[cell.x];
-      sz = (cell.w & 1 ? Hq - ns : 0) + (cell.w & 2 ? ns : 0);
+    if (p < n_valid) {
+      const int i = (int)(keys[p] & 0xffffffffu);
+      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of);
+      const int ns = n_sparse_of[c.x];
+      sz = ((c.w & 1) ? Hq - ns : 0) + ((c.w & 2) ? ns : 0);
+      // packed cell: seq (20 bits) | q_tile (20 bits) | cost (22 bits) | mode (2 bits)
+      keys[p] = ((uint64_t)c.x << 44) | ((uint64_t)c.y << 24) | ((uint64_t)c.z << 2) |
+                (uint64_t)c.w;
     }
     int tot;
     const int ex = block_exclusive_scan(sz, &tot, scratch);
-    if (i < n_valid) a.cell_off[i] = item_carry + ex;
-    item_carry += tot;
+    if (p < n_valid) cell_off[p] = items_total + ex;
+    items_total += tot;
   }
-  __threadfence();
   __syncthreads();
-  for (int i = tid; i < n_valid; i += kPlanThreads) {
-    const int4 cell = a.sorted[i];
-    int at = a.cell_off[i];
+
+  // Phase 5: expansion, heads of a cell in ascending order.
+  for (int p = tid; p < n_valid; p += kPlanThreads) {
+    const uint64_t pk = keys[p];
+    const int b = (int)(pk >> 44), qt = (int)((pk >> 24) & 0xfffff);
+    const int cost = (int)((pk >> 2) & 0x3fffff), mode = (int)(pk & 3);
+    const HeadMask m = masks[b];
+    int at = cell_off[p];
     for (int h = 0; h < Hq; ++h) {
-      const int mode = a.route[(int64_t)cell.x * Hq + h] != 0 ? 2 : 1;
-      if (cell.w & mode) a.items[at++] = int4{cell.x, h, cell.y, cell.z};
+      const bool sp = ((h < 64 ? (m.lo >> h) : (m.hi >> (h - 64))) & 1ull) != 0;
+      if (mode & (sp ? 2 : 1)) a.items[at++] = int4{b, h, qt, cost};
     }
   }
   if (tid == 0) {
-    a.counters[0] = item_carry;
-    a.counters[1] = 0;
-    if (a.n_items_out) *a.n_items_out = item_carry;
+    a.counters[0] = items_total;
+    a.counters[1] = 0;  // queue head
+    a.counters[2] = 0;  // workgroups finished
+    if (a.n_items_out) *a.n_items_out = items_total;
   }
 }
-
-__global__ void reset_queue_kernel(int32_t* queue) { *queue = 0; }
 
 }  // namespace
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
   plan_kernel<<<1, kPlanThreads, 0, stream>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_reset_queue(int32_t* queue, hipStream_t stream) {
-  reset_queue_kernel<<<1, 1, 0, stream>>>(queue);
   return hipGetLastError();
 }
 

@@ -3,12 +3,16 @@
 // r = 0 full attention, r = 1 sparse attention; about 0.27M parameters per layer for an
 // 8B model, section 2.2).
 //
-// Step 1 (route_pool): each sequence is cut into `chunks` row ranges; one workgroup sums
-// the key states of one range column by column in fp32, in a fixed order, and writes the
-// partial sums.  This is a streaming read of the key states (HBM bound).
-// Step 2 (route_mlp): one workgroup per sequence adds the partials in chunk order, divides
-// by the length (an empty sequence pools to zero), runs W1/SiLU/W2 with wavefront dot
-// products and thresholds z > 0.  No float atomics anywhere, so the bits are reproducible.
+// Four short launches, all deterministic (fixed summation orders, no float atomics):
+//   route_pool    grid (row chunks, column chunks, batch): every workgroup sums the key
+//                 states of its rows for 16 column groups in fp32 and writes one partial
+//                 row; a streaming read of the key states with 8 loads in flight per
+//                 thread (HBM bound).
+//   route_mean    adds the partial rows of each column in chunk order and divides by the
+//                 length (an empty sequence pools to zero).
+//   route_hidden  h = SiLU(W1 x + b1), eight hidden units per workgroup, wavefront dot
+//                 products over the key features.
+//   route_out     z = W2 h + b2, r = (z > 0).
 #include "ea_device.h"
 #include "ea_internal.h"
 
@@ -17,71 +21,101 @@ namespace ea {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kMlpThreads = 256;
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 
 template <typename T, int VW>
-__device__ __forceinline__ void add_row(const T* p, float* acc) {
+__device__ __forceinline__ void load_row(const T* p, u32x4* raw, T* vals) {
   if constexpr (VW * sizeof(T) == 16) {
-    u32x4 raw = *(const u32x4*)p;
-    const T* vals = (const T*)&raw;
-#pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] += to_f32(vals[e]);
+    *raw = *(const u32x4*)p;
   } else {
 #pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] += to_f32(p[e]);
+    for (int e = 0; e < VW; ++e) vals[e] = p[e];
   }
 }
 
-// One workgroup sums rows [r0, r1) of sequence `blockIdx.y` (chunk `blockIdx.x`), VW
-// consecutive columns per thread.  When a row has fewer column groups than threads,
-// several threads take interleaved rows of the same group and their sums are added in
-// row-offset order through LDS.
+constexpr int kGroupsPerBlock = 16;                          // column groups per workgroup
+constexpr int kRowLanes = kPoolThreads / kGroupsPerBlock;    // rows summed side by side
+constexpr int kUnroll = 8;                                   // loads in flight per thread
+
+// Sums rows [r0, r1) of sequence blockIdx.z for the VW-wide column groups
+// blockIdx.y*16 .. +15.  Thread (row lane tr, group tg) adds rows r0+tr, r0+tr+16, ...;
+// the 16 row-lane sums of a group are then added in row-lane order.
 template <typename T, int VW>
 __global__ __launch_bounds__(kPoolThreads) void route_pool(const T* __restrict__ ks, int kv_dim,
                                                            const int32_t* __restrict__ cu,
-                                                           int chunks,
+                                                           int row_chunks,
                                                            float* __restrict__ partial) {
-  __shared__ float red[kPoolThreads * VW];
-  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[kRowLanes][kGroupsPerBlock * VW + 1];
+  const int rc = blockIdx.x, b = blockIdx.z, tid = threadIdx.x;
+  const int tg = tid % kGroupsPerBlock, tr = tid / kGroupsPerBlock;
+  const int groups = kv_dim / VW;
+  const int grp = blockIdx.y * kGroupsPerBlock + tg;
   const int64_t s0 = cu[b];
   const int64_t len = (int64_t)cu[b + 1] - s0;
-  const int64_t r0 = len * chunk / chunks, r1 = len * (chunk + 1) / chunks;
-  const int groups = kv_dim / VW;  // column groups per row
-  float* out = partial + ((int64_t)b * chunks + chunk) * kv_dim;
+  const int64_t r0 = len * rc / row_chunks, r1 = len * (rc + 1) / row_chunks;
   float acc[VW];
-  if (groups <= kPoolThreads) {
-    const int rows_per_step = kPoolThreads / groups;
-    const int grp = tid % groups, roff = tid / groups;
-    const bool on = roff < rows_per_step;
 #pragma unroll
-    for (int e = 0; e < VW; ++e) acc[e] = 0.f;
-    if (on)
-      for (int64_t r = r0 + roff; r < r1; r += rows_per_step)
-        add_row<T, VW>(ks + (s0 + r) * kv_dim + (int64_t)grp * VW, acc);
+  for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+  if (grp < groups) {
+    const T* base = ks + s0 * kv_dim + (int64_t)grp * VW;
+    int64_t r = r0 + tr;
+    for (; r + (kUnroll - 1) * kRowLanes < r1; r += kUnroll * kRowLanes) {
+      u32x4 raw[kUnroll];
+      T vals[kUnroll][VW];
 #pragma unroll
-    for (int e = 0; e < VW; ++e) red[tid * VW + e] = on ? acc[e] : 0.f;
-    __syncthreads();
-    if (tid < groups) {
+      for (int u = 0; u < kUnroll; ++u)
+        load_row<T, VW>(base + (r + u * kRowLanes) * kv_dim, &raw[u], vals[u]);
 #pragma unroll
-      for (int e = 0; e < VW; ++e) acc[e] = 0.f;
-      for (int ro = 0; ro < rows_per_step; ++ro)
+      for (int u = 0; u < kUnroll; ++u) {
+        const T* v = (VW * sizeof(T) == 16) ? (const T*)&raw[u] : vals[u];
 #pragma unroll
-        for (int e = 0; e < VW; ++e) acc[e] += red[(ro * groups + tid) * VW + e];
-#pragma unroll
-      for (int e = 0; e < VW; ++e) out[(int64_t)tid * VW + e] = acc[e];
+        for (int e = 0; e < VW; ++e) acc[e] += to_f32(v[e]);
+      }
     }
-  } else {
-    for (int grp = tid; grp < groups; grp += kPoolThreads) {
+    for (; r < r1; r += kRowLanes) {
+      u32x4 raw;
+      T vals[VW];
+      load_row<T, VW>(base + r * kv_dim, &raw, vals);
+      const T* v = (VW * sizeof(T) == 16) ? (const T*)&raw : vals;
 #pragma unroll
-      for (int e = 0; e < VW; ++e) acc[e] = 0.f;
-      for (int64_t r = r0; r < r1; ++r)
-        add_row<T, VW>(ks + (s0 + r) * kv_dim + (int64_t)grp * VW, acc);
-#pragma unroll
-      for (int e = 0; e < VW; ++e) out[(int64_t)grp * VW + e] = acc[e];
+      for (int e = 0; e < VW; ++e) acc[e] += to_f32(v[e]);
     }
+  }
+#pragma unroll
+  for (int e = 0; e < VW; ++e) red[tr][tg * VW + e] = acc[e];
+  __syncthreads();
+  const int col_base = blockIdx.y * kGroupsPerBlock * VW;
+  for (int c = tid; c < kGroupsPerBlock * VW; c += kPoolThreads) {
+    if (col_base + c >= kv_dim) continue;
+    float s = 0.f;
+    for (int t = 0; t < kRowLanes; ++t) s += red[t][c];
+    partial[((int64_t)b * row_chunks + rc) * kv_dim + col_base + c] = s;
+  }
+}
+
+// x[b, c] = (sum over row chunks of partial[b, chunk, c]) / len_b; 16 columns x 16
+// chunk lanes per workgroup, the lane sums added in lane order.
+__global__ __launch_bounds__(256) void route_mean(const float* __restrict__ partial,
+                                                  int row_chunks, const int32_t* __restrict__ cu,
+                                                  int kv_dim, float* __restrict__ x) {
+  __shared__ float red[16][17];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int col = blockIdx.x * 16 + tid % 16, lane = tid / 16;
+  float s = 0.f;
+  if (col < kv_dim) {
+    const float* p = partial + (int64_t)b * row_chunks * kv_dim + col;
+#pragma unroll 8
+    for (int ch = lane; ch < row_chunks; ch += 16) s += p[(int64_t)ch * kv_dim];
+  }
+  red[lane][tid % 16] = s;
+  __syncthreads();
+  if (tid < 16 && col < kv_dim) {
+    float t = 0.f;
+    for (int l = 0; l < 16; ++l) t += red[l][tid];
+    const int len = cu[b + 1] - cu[b];
+    x[(int64_t)b * kv_dim + col] = len > 0 ? t / (float)len : 0.f;
   }
 }
 
@@ -92,63 +126,83 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kMlpThreads) void route_mlp(
-    const float* __restrict__ partial, int chunks, const int32_t* __restrict__ cu, int kv_dim,
-    const float* __restrict__ w1, const float* __restrict__ b1, int hidden,
-    const float* __restrict__ w2, const float* __restrict__ b2, int n_heads,
-    float* __restrict__ logits, uint8_t* __restrict__ route) {
-  extern __shared__ float sm[];
-  float* x = sm;               // [kv_dim]
-  float* hv = sm + kv_dim;     // [hidden]
-  const int b = blockIdx.x;
-  const int len = cu[b + 1] - cu[b];
-  const float inv_len = len > 0 ? 1.0f / (float)len : 0.0f;
-  for (int c = threadIdx.x; c < kv_dim; c += kMlpThreads) {
-    float s = 0.f;
-    for (int ch = 0; ch < chunks; ++ch) s += partial[((int64_t)b * chunks + ch) * kv_dim + c];
-    x[c] = len > 0 ? s * inv_len : 0.f;
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kMlpThreads / 64;
-  for (int j = wave; j < hidden; j += nw) {
-    float s = 0.f;
-    for (int c = lane; c < kv_dim; c += 64) s += w1[(int64_t)j * kv_dim + c] * x[c];
-    const float u = wave_sum(s) + b1[j];
-    if (lane == 0) hv[j] = u / (1.0f + expf(-u));   // SiLU
-  }
-  __syncthreads();
-  for (int h = wave; h < n_heads; h += nw) {
-    float s = 0.f;
-    for (int j = lane; j < hidden; j += 64) s += w2[(int64_t)h * hidden + j] * hv[j];
-    const float z = wave_sum(s) + b2[h];
-    if (lane == 0) {
-      if (logits) logits[(int64_t)b * n_heads + h] = z;
-      route[(int64_t)b * n_heads + h] = z > 0.f ? 1 : 0;
+// One wavefront per output: the lanes stride over the inputs with every load of a lane
+// issued before the first add (one memory round trip per output), then a butterfly sum.
+template <int kPerLane>
+__device__ __forceinline__ float wave_dot(const float* __restrict__ w, const float* __restrict__ x,
+                                          int n) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+  for (int base = 0; base < n; base += 64 * kPerLane) {
+    float wv[kPerLane], xv[kPerLane];
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+      const int c = base + u * 64 + lane;
+      wv[u] = c < n ? w[c] : 0.f;
+      xv[u] = c < n ? x[c] : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) s += wv[u] * xv[u];
+  }
+  return wave_sum(s);
+}
+
+constexpr int kWavesPerBlock = 4;
+
+// hv[b, j] = SiLU(W1[j, :] . x[b, :] + b1[j]); one wavefront per hidden unit.
+__global__ __launch_bounds__(256) void route_hidden(const float* __restrict__ x, int kv_dim,
+                                                    const float* __restrict__ w1,
+                                                    const float* __restrict__ b1, int hidden,
+                                                    float* __restrict__ hv) {
+  const int b = blockIdx.y;
+  const int j = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (j >= hidden) return;
+  const float u = wave_dot<16>(w1 + (int64_t)j * kv_dim, x + (int64_t)b * kv_dim, kv_dim) + b1[j];
+  if ((threadIdx.x & 63) == 0) hv[(int64_t)b * hidden + j] = u / (1.0f + expf(-u));  // SiLU
+}
+
+// z[b, h] = W2[h, :] . hv[b, :] + b2[h]; route = z > 0 (z == 0 routes to full); one
+// wavefront per head.
+__global__ __launch_bounds__(256) void route_out(const float* __restrict__ hv, int hidden,
+                                                 const float* __restrict__ w2,
+                                                 const float* __restrict__ b2, int n_heads,
+                                                 float* __restrict__ logits,
+                                                 uint8_t* __restrict__ route) {
+  const int b = blockIdx.y;
+  const int h = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (h >= n_heads) return;
+  const float z = wave_dot<4>(w2 + (int64_t)h * hidden, hv + (int64_t)b * hidden, hidden) + b2[h];
+  if ((threadIdx.x & 63) == 0) {
+    if (logits) logits[(int64_t)b * n_heads + h] = z;
+    route[(int64_t)b * n_heads + h] = z > 0.f ? 1 : 0;
   }
 }
 
 }  // namespace
 
 int router_chunks(int32_t batch) {
-  int c = 512 / (batch > 0 ? batch : 1);
-  return c < 8 ? 8 : (c > 256 ? 256 : c);
+  // about 1024 pooling workgroups in all (8 column chunks of a 1024-wide bf16 row)
+  int c = 128 / (batch > 0 ? batch : 1);
+  return c < 4 ? 4 : c;
 }
 
 hipError_t launch_route(const void* ks, int kdt, int kv_dim, const int32_t* cu, int batch,
                         const float* w1, const float* b1, int hidden, const float* w2,
                         const float* b2, int n_heads_q, float* logits, uint8_t* route,
-                        float* partial, int chunks, hipStream_t stream) {
-  dim3 grid(chunks, batch);
+                        float* partial, int chunks, float* x, float* hv, hipStream_t stream) {
+  const bool vec = kdt == 0 ? (kv_dim % 8 == 0) : (kv_dim % 4 == 0);
+  const int vw = vec ? (kdt == 0 ? 8 : 4) : 1;
+  const int groups = kv_dim / vw;
+  dim3 grid(chunks, (groups + kGroupsPerBlock - 1) / kGroupsPerBlock, batch);
   if (kdt == 0) {
-    if (kv_dim % 8 == 0)
+    if (vec)
       route_pool<__bf16, 8><<<grid, kPoolThreads, 0, stream>>>((const __bf16*)ks, kv_dim, cu,
                                                                chunks, partial);
     else
       route_pool<__bf16, 1><<<grid, kPoolThreads, 0, stream>>>((const __bf16*)ks, kv_dim, cu,
                                                                chunks, partial);
   } else {
-    if (kv_dim % 4 == 0)
+    if (vec)
       route_pool<float, 4><<<grid, kPoolThreads, 0, stream>>>((const float*)ks, kv_dim, cu,
                                                               chunks, partial);
     else
@@ -157,9 +211,13 @@ hipError_t launch_route(const void* ks, int kdt, int kv_dim, const int32_t* cu, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(float) * ((size_t)kv_dim + (size_t)hidden);
-  route_mlp<<<batch, kMlpThreads, lds, stream>>>(partial, chunks, cu, kv_dim, w1, b1, hidden, w2,
-                                                 b2, n_heads_q, logits, route);
+  route_mean<<<dim3((kv_dim + 15) / 16, batch), 256, 0, stream>>>(partial, chunks, cu, kv_dim, x);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  route_hidden<<<dim3((hidden + kWavesPerBlock - 1) / kWavesPerBlock, batch), 256, 0, stream>>>(
+      x, kv_dim, w1, b1, hidden, hv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  route_out<<<dim3((n_heads_q + kWavesPerBlock - 1) / kWavesPerBlock, batch), 256, 0, stream>>>(
+      hv, hidden, w2, b2, n_heads_q, logits, route);
   return hipGetLastError();
 }
 

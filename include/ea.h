@@ -106,6 +106,8 @@ ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
  * Order: cost descending, ties by (b, j, h) ascending -- longest first, so long full-head
  * items start early and short sparse items fill the tail; sibling heads of one q-tile
  * are adjacent.  The order is unique, so the list is reproducible bit for bit.
+ * Limits (the planner runs in one workgroup): batch <= 1024, n_heads_q <= 128 and
+ * 2 * batch * ceil(max_seqlen / bm) <= 8192; beyond them EA_ERR_UNSUPPORTED.
  * worklist_out  [capacity, 4] int32 with capacity >= batch * n_heads_q * ceil(max_seqlen/bm)
  * n_items_out   device int32 (nullable): item count.  n_items_host (nullable): if given,
  *               the call synchronises `stream` and stores the count there.
@@ -151,6 +153,9 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
  * (same dt, head_dim, sink, window, route and cu_seqlens).  worklist and n_items are
  * device pointers.  grid_blocks sets the number of persistent workgroups (0 = one per
  * resident slot on the device); the output does not depend on it.
+ * The workgroups take items through two queue counters kept in the workspace: they are
+ * zeroed by ea_build_worklist and ea_hybrid_attn_prefill and left at zero by every
+ * completed run, so pass a workspace that has been through one of those calls.
  */
 ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
                              const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,

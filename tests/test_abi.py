@@ -71,6 +71,9 @@ def prefill(**kw):
     (dict(o=FAKE), ea.EA_ERR_INVALID_ARG),
     (dict(max_seqlen=1 << 24), ea.EA_ERR_UNSUPPORTED),
     (dict(ws_bytes=16), ea.EA_ERR_WORKSPACE),
+    (dict(batch=1025, max_seqlen=8), ea.EA_ERR_UNSUPPORTED),
+    (dict(hq=130, hkv=2), ea.EA_ERR_UNSUPPORTED),
+    (dict(max_seqlen=600000), ea.EA_ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects(kw, status):
     assert prefill(**kw) == status
@@ -93,7 +96,7 @@ def test_route_and_worklist_reject():
     ok = dict(ks=FAKE, kdt=ea.EA_BF16, kv=1024, cu=FAKE, batch=1, w1=FAKE, b1=FAKE, hid=256,
               w2=FAKE, b2=FAKE, hq=32, logits=None, r=FAKE, ws=FAKE, wsb=1 << 30, st=None)
     for kw, st in [(dict(ks=None), 1), (dict(r=None), 1), (dict(kv=0), 1), (dict(kdt=3), 1),
-                   (dict(kv=16384, hid=256), 2), (dict(ks=FAKE + 4), 1), (dict(wsb=0), 3)]:
+                   (dict(ks=FAKE + 4), 1), (dict(wsb=0), 3)]:
         a = dict(ok)
         a.update(kw)
         assert L.ea_route(*a.values()) == st, kw
