@@ -67,6 +67,11 @@ hipError_t cu_count(int* out) {
   return hipSuccess;
 }
 
+// Upper bound on the number of work items for these sizes.
+int64_t item_bound(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int bm) {
+  return (int64_t)batch * n_heads_q * ceil_div64(max_seqlen, bm);
+}
+
 // The planner holds its state in one workgroup's LDS: bound the cells, sequences, heads.
 ea_status check_plan_limits(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int bm) {
   if (batch > kPlanMaxBatch) return fail(EA_ERR_UNSUPPORTED, "more than 1024 sequences");
@@ -143,7 +148,7 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
                        const int32_t* cu, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
                        int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window,
                        float scale, float* lse, const int4* items, const int32_t* n_items,
-                       int32_t* queue, int grid_blocks, hipStream_t stream) {
+                       int64_t item_cap, int32_t* queue, int grid_blocks, hipStream_t stream) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -153,6 +158,7 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
   a.route = route;
   a.items = items;
   a.n_items = n_items;
+  a.item_cap = (int32_t)(item_cap < INT32_MAX ? item_cap : INT32_MAX);
   a.queue = queue;
   a.lse = lse;
   a.batch = batch;
@@ -263,8 +269,9 @@ ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
 ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int32_t batch,
                             int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
                             ea_dtype dt, int32_t head_dim, int32_t* worklist_out,
-                            int32_t* n_items_out, int32_t* n_items_host, void* workspace,
-                            size_t ws_bytes, void* stream) {
+                            int64_t worklist_capacity, int32_t* n_items_out,
+                            int32_t* n_items_host, void* workspace, size_t ws_bytes,
+                            void* stream) {
   g_last_error.clear();
   if (!route || !cu_seqlens || !worklist_out || !workspace)
     return fail(EA_ERR_INVALID_ARG, "null pointer argument");
@@ -277,6 +284,8 @@ ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int
     return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   ea_status s = check_plan_limits(batch, max_seqlen, n_heads_q, bm);
   if (s != EA_OK) return s;
+  if (worklist_capacity < item_bound(batch, max_seqlen, n_heads_q, bm))
+    return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen / bm)");
   WsLayout L;
   if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
@@ -301,14 +310,16 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
                                  int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
                                  int32_t head_dim, const uint8_t* route, int32_t sink,
                                  int32_t window, float scale, float* lse_out,
-                                 int32_t* worklist_out, void* workspace, size_t ws_bytes,
-                                 void* stream) {
+                                 int32_t* worklist_out, int64_t worklist_capacity,
+                                 void* workspace, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   int bm = 0, bn = 0;
   ea_status s = check_attn_args(q, k, v, o, dt, cu_seqlens, batch, max_seqlen, n_heads_q,
                                 n_heads_kv, head_dim, route, sink, window, scale, workspace,
                                 &bm, &bn);
   if (s != EA_OK) return s;
+  if (worklist_out && worklist_capacity < item_bound(batch, max_seqlen, n_heads_q, bm))
+    return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen / bm)");
   if (cu_seqlens_host) {
     s = check_cu_host(cu_seqlens_host, batch, max_seqlen);
     if (s != EA_OK) return s;
@@ -330,15 +341,17 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
   s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn, items,
                    nullptr, L, ws, st);
   if (s != EA_OK) return s;
+  const int64_t cap = worklist_out ? worklist_capacity : L.item_cap;
   return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
-                      sink, window, scale, lse_out, items, counters, counters + 1, 0, st);
+                      sink, window, scale, lse_out, items, counters, cap, counters + 1, 0, st);
 }
 
 ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
                              const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                              int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                              const uint8_t* route, int32_t sink, int32_t window, float scale,
-                             float* lse_out, const int32_t* worklist, const int32_t* n_items,
+                             float* lse_out, const int32_t* worklist,
+                             int64_t worklist_capacity, const int32_t* n_items,
                              int32_t grid_blocks, void* workspace, size_t ws_bytes,
                              void* stream) {
   g_last_error.clear();
@@ -349,6 +362,7 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
   if (s != EA_OK) return s;
   if (!worklist || !n_items) return fail(EA_ERR_INVALID_ARG, "null work list or item count");
   if (grid_blocks < 0) return fail(EA_ERR_INVALID_ARG, "grid_blocks < 0");
+  if (worklist_capacity < 0) return fail(EA_ERR_INVALID_ARG, "worklist_capacity < 0");
   WsLayout L;
   if (!ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
@@ -356,8 +370,8 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
   char* ws = (char*)workspace;
   int32_t* counters = (int32_t*)(ws + L.counters);
   return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
-                      sink, window, scale, lse_out, (const int4*)worklist, n_items, counters + 1,
-                      grid_blocks, (hipStream_t)stream);
+                      sink, window, scale, lse_out, (const int4*)worklist, n_items,
+                      worklist_capacity, counters + 1, grid_blocks, (hipStream_t)stream);
 }
 
 }  // extern "C"

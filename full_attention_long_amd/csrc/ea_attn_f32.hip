@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int row = tid / kParts, part = tid % kParts;
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, group = Hq / Hkv;
-  const int n_items = *a.n_items;
+  const int n_items = min(*a.n_items, a.item_cap);
   const int total_tokens = a.cu[a.batch];
 
   for (;;) {
@@ -59,6 +59,12 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     if (it >= n_items) break;
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, qt = item.z;
+    // an item outside this call's sizes is skipped (the test is uniform across the
+    // workgroup; the barrier keeps s_item stable until every thread has read it)
+    if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b]) {
+      __syncthreads();
+      continue;
+    }
     const int seq0 = a.cu[b];
     const int len = a.cu[b + 1] - seq0;
     const int m0 = qt * BM, m1 = min(m0 + BM, len);

@@ -34,6 +34,10 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// `x` read from the first active lane: tells the compiler a wavefront-uniform value is
+// uniform, so it can live in a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Value of `x` held by lane (lane ^ 32) of the wavefront.
 __device__ __forceinline__ float xor32(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,

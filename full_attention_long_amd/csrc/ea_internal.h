@@ -9,9 +9,9 @@
 namespace ea {
 
 // ---------------------------------------------------------------- tile shapes
-// bf16 path: 4 wavefronts x 32 query rows = 128-row q-tiles, 64-key tiles.
+// bf16 path: 8 wavefronts x 32 query rows = 256-row q-tiles, 64-key tiles.
 // fp32 path: 64-row q-tiles, 32-key tiles.
-constexpr int kBf16BM = 128;
+constexpr int kBf16BM = 256;
 constexpr int kBf16BN = 64;
 constexpr int kF32BM = 64;
 constexpr int kF32BN = 32;
@@ -66,6 +66,7 @@ struct AttnArgs {
   const uint8_t* route;
   const int4* items;
   const int32_t* n_items;
+  int32_t item_cap;       // never read items[item_cap] or beyond
   int32_t* queue;         // [0] queue head, [1] workgroups done; zero on entry, re-zeroed
                           // by the last workgroup to finish
   float* lse;

@@ -49,13 +49,15 @@ def lib():
     L.ea_last_error.restype = ctypes.c_char_p
     L.ea_route.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P, sz, P]
     L.ea_route.restype = i32
-    L.ea_build_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
+    i64 = ctypes.c_int64
+    L.ea_build_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, i64, P, P, P,
+                                    sz, P]
     L.ea_build_worklist.restype = i32
     L.ea_hybrid_attn_prefill.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P,
-                                         i32, i32, f32, P, P, P, sz, P]
+                                         i32, i32, f32, P, P, i64, P, sz, P]
     L.ea_hybrid_attn_prefill.restype = i32
     L.ea_hybrid_attn_run.argtypes = [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
-                                     f32, P, P, P, i32, P, sz, P]
+                                     f32, P, P, i64, P, i32, P, sz, P]
     L.ea_hybrid_attn_run.restype = i32
     _lib = L
     return L
@@ -80,6 +82,13 @@ def _ptr(t):
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+def _capacity(worklist):
+    """Work-list capacity in items: rows of an int32 [n, 4] tensor."""
+    if worklist is None or isinstance(worklist, int):
+        return 0
+    return worklist.numel() // 4
 
 
 def _stream(stream):
@@ -129,7 +138,7 @@ def build_worklist(route_bits, cu_seqlens, max_seqlen, n_heads_q, sink, window, 
     n_host = ctypes.c_int32(-1)
     _check(lib().ea_build_worklist(_ptr(route_bits), _ptr(cu_seqlens), batch, max_seqlen,
                                    n_heads_q, sink, window, int(dt), head_dim,
-                                   _ptr(worklist_out), _ptr(n_items_out),
+                                   _ptr(worklist_out), _capacity(worklist_out), _ptr(n_items_out),
                                    ctypes.byref(n_host) if want_count else None,
                                    _ptr(workspace),
                                    workspace.numel() * workspace.element_size(),
@@ -149,7 +158,8 @@ def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, wi
                                         _ptr(cu_seqlens), host, batch, max_seqlen,
                                         q.shape[1], k.shape[1], q.shape[2], _ptr(route_bits),
                                         sink, window, float(scale), _ptr(lse_out),
-                                        _ptr(worklist_out), _ptr(workspace),
+                                        _ptr(worklist_out), _capacity(worklist_out),
+                                        _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
 
@@ -161,7 +171,8 @@ def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window
     _check(lib().ea_hybrid_attn_run(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype),
                                     _ptr(cu_seqlens), batch, max_seqlen, q.shape[1], k.shape[1],
                                     q.shape[2], _ptr(route_bits), sink, window, float(scale),
-                                    _ptr(lse_out), _ptr(worklist), _ptr(n_items),
+                                    _ptr(lse_out), _ptr(worklist), _capacity(worklist),
+                                    _ptr(n_items),
                                     int(grid_blocks), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)))

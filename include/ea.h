@@ -108,7 +108,8 @@ ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
  * are adjacent.  The order is unique, so the list is reproducible bit for bit.
  * Limits (the planner runs in one workgroup): batch <= 1024, n_heads_q <= 128 and
  * 2 * batch * ceil(max_seqlen / bm) <= 8192; beyond them EA_ERR_UNSUPPORTED.
- * worklist_out  [capacity, 4] int32 with capacity >= batch * n_heads_q * ceil(max_seqlen/bm)
+ * worklist_out       [worklist_capacity, 4] int32; worklist_capacity (in items) must be at
+ *                    least batch * n_heads_q * ceil(max_seqlen / bm), else EA_ERR_INVALID_ARG
  * n_items_out   device int32 (nullable): item count.  n_items_host (nullable): if given,
  *               the call synchronises `stream` and stores the count there.
  * dt, head_dim select (bm, bn) as ea_tile_config.  max_seqlen bounds every sequence.
@@ -116,7 +117,8 @@ ea_status ea_route(const void* key_states, ea_dtype kdt, int32_t kv_dim,
 ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int32_t batch,
                             int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
                             ea_dtype dt, int32_t head_dim,
-                            int32_t* worklist_out, int32_t* n_items_out, int32_t* n_items_host,
+                            int32_t* worklist_out, int64_t worklist_capacity,
+                            int32_t* n_items_out, int32_t* n_items_host,
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -135,7 +137,8 @@ ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int
  * scale <= 0 selects 1/sqrt(head_dim)
  * route        [batch, n_heads_q] uint8 (0 full, nonzero sparse)
  * lse_out      nullable, [n_heads_q, T] fp32
- * worklist_out nullable, receives the work list (see ea_build_worklist) for inspection
+ * worklist_out nullable, receives the work list (see ea_build_worklist) for inspection;
+ *              worklist_capacity is its size in items (same bound as ea_build_worklist)
  * o must not overlap q, k or v.  Results do not depend on scheduling: every output
  * element is written by exactly one work item.
  */
@@ -145,13 +148,15 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
                                  int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
                                  int32_t head_dim, const uint8_t* route, int32_t sink,
                                  int32_t window, float scale, float* lse_out,
-                                 int32_t* worklist_out, void* workspace, size_t ws_bytes,
-                                 void* stream);
+                                 int32_t* worklist_out, int64_t worklist_capacity,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * The attention half of ea_hybrid_attn_prefill on a work list made by ea_build_worklist
  * (same dt, head_dim, sink, window, route and cu_seqlens).  worklist and n_items are
- * device pointers.  grid_blocks sets the number of persistent workgroups (0 = one per
+ * device pointers; worklist_capacity is the work list's size in items (the kernels never
+ * read past min(*n_items, worklist_capacity), and skip items that name a sequence, head
+ * or q-tile outside the call's sizes).  grid_blocks sets the number of persistent workgroups (0 = one per
  * resident slot on the device); the output does not depend on it.
  * The workgroups take items through two queue counters kept in the workspace: they are
  * zeroed by ea_build_worklist and ea_hybrid_attn_prefill and left at zero by every
@@ -161,7 +166,8 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
                              const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                              int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                              const uint8_t* route, int32_t sink, int32_t window, float scale,
-                             float* lse_out, const int32_t* worklist, const int32_t* n_items,
+                             float* lse_out, const int32_t* worklist,
+                             int64_t worklist_capacity, const int32_t* n_items,
                              int32_t grid_blocks, void* workspace, size_t ws_bytes,
                              void* stream);
 

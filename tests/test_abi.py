@@ -30,8 +30,8 @@ def test_exports_match_header():
 
 
 def test_tile_config_and_workspace():
-    assert ea.tile_config(ea.EA_BF16, 128) == (128, 64)
-    assert ea.tile_config(ea.EA_BF16, 64) == (128, 64)
+    assert ea.tile_config(ea.EA_BF16, 128) == (256, 64)
+    assert ea.tile_config(ea.EA_BF16, 64) == (256, 64)
     assert ea.tile_config(ea.EA_F32, 64) == (64, 32)
     assert ea.tile_config(ea.EA_F32, 96) == (0, 0)
     assert ea.tile_config(7, 128) == (0, 0)
@@ -48,7 +48,7 @@ def test_tile_config_and_workspace():
 def prefill(**kw):
     args = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, dt=ea.EA_BF16,
                 cu=FAKE, cu_host=None, batch=1, max_seqlen=128, hq=4, hkv=2, d=128,
-                route=FAKE, sink=4, window=16, scale=0.0, lse=None, wl=None, ws=FAKE,
+                route=FAKE, sink=4, window=16, scale=0.0, lse=None, wl=None, wlcap=0, ws=FAKE,
                 ws_bytes=1 << 30, stream=None)
     args.update(kw)
     return ea.lib().ea_hybrid_attn_prefill(*args.values())
@@ -73,7 +73,8 @@ def prefill(**kw):
     (dict(ws_bytes=16), ea.EA_ERR_WORKSPACE),
     (dict(batch=1025, max_seqlen=8), ea.EA_ERR_UNSUPPORTED),
     (dict(hq=130, hkv=2), ea.EA_ERR_UNSUPPORTED),
-    (dict(max_seqlen=600000), ea.EA_ERR_UNSUPPORTED),
+    (dict(max_seqlen=1100000), ea.EA_ERR_UNSUPPORTED),
+    (dict(wl=FAKE, wlcap=4 * 1 - 1), ea.EA_ERR_INVALID_ARG),
 ])
 def test_prefill_rejects(kw, status):
     assert prefill(**kw) == status
@@ -101,9 +102,9 @@ def test_route_and_worklist_reject():
         a.update(kw)
         assert L.ea_route(*a.values()) == st, kw
     okw = dict(r=FAKE, cu=FAKE, batch=1, maxlen=100, hq=4, sink=0, win=1, dt=0, d=128, wl=FAKE,
-               nout=None, nhost=None, ws=FAKE, wsb=1 << 30, st=None)
+               wlcap=1 << 20, nout=None, nhost=None, ws=FAKE, wsb=1 << 30, st=None)
     for kw, st in [(dict(wl=None), 1), (dict(win=0), 1), (dict(d=80), 2), (dict(dt=9), 1),
-                   (dict(wsb=8), 3), (dict(maxlen=1 << 26), 2)]:
+                   (dict(wsb=8), 3), (dict(maxlen=1 << 26), 2), (dict(wlcap=3), 1)]:
         a = dict(okw)
         a.update(kw)
         assert L.ea_build_worklist(*a.values()) == st, kw
@@ -112,12 +113,15 @@ def test_route_and_worklist_reject():
 def test_run_rejects():
     L = ea.lib()
     base = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 0, FAKE, 1, 128, 4, 2, 128,
-            FAKE, 0, 16, 0.0, None, FAKE, FAKE, 0, FAKE, 1 << 30, None]
+            FAKE, 0, 16, 0.0, None, FAKE, 1 << 20, FAKE, 0, FAKE, 1 << 30, None]
     a = list(base)
     a[16] = None  # work list
     assert L.ea_hybrid_attn_run(*a) == ea.EA_ERR_INVALID_ARG
     a = list(base)
-    a[18] = -1    # grid_blocks
+    a[19] = -1    # grid_blocks
+    assert L.ea_hybrid_attn_run(*a) == ea.EA_ERR_INVALID_ARG
+    a = list(base)
+    a[17] = -1    # worklist_capacity
     assert L.ea_hybrid_attn_run(*a) == ea.EA_ERR_INVALID_ARG
 
 

@@ -31,7 +31,7 @@ def _gpu():
 
 
 def oracle_worklist(route, lens, hq, sink, window, dt, d):
-    bm, bn = {(ea.EA_BF16, 64): (128, 64), (ea.EA_BF16, 128): (128, 64),
+    bm, bn = {(ea.EA_BF16, 64): (256, 64), (ea.EA_BF16, 128): (256, 64),
               (ea.EA_F32, 64): (64, 32), (ea.EA_F32, 128): (64, 32)}[(dt, d)]
     assert ea.tile_config(dt, d) == (bm, bn)
     return oracle.worklist(route.numpy(), inputs.cu_seqlens(lens).numpy(), hq, sink, window, bm, bn)
@@ -109,7 +109,8 @@ def test_determinism_across_grid_sizes():
     cnt = torch.empty(1, dtype=torch.int32, device="cuda")
     n = ea.build_worklist(droute, cu, max(lens), hq, 32, 256, ea.EA_BF16, d, wl, ws,
                           n_items_out=cnt)
-    assert n == hq * (12 + 8)
+    bm, _ = ea.tile_config(ea.EA_BF16, d)
+    assert n == hq * sum(-(-L // bm) for L in lens)
     outs = []
     for grid in (1, 7, 0, 1000):
         o = torch.empty_like(dq)
