@@ -164,3 +164,47 @@ def test_ragged4_sampled_rows():
     route = inputs.bernoulli_route(w, len(lens))
     rows = inputs.sampled_rows(w, lens, 512)
     check_case(q, k, v, lens, route, w.sink, w.window, rows=rows.numpy(), what=w.name)
+
+
+@pytest.mark.parametrize("mode", ["all_full", "all_sparse"])
+def test_ragged4_degenerate_masks(mode):
+    w = inputs.WORKLOADS["ragged4"]
+    lens = inputs.lengths(w)
+    q, k, v = inputs.qkv(w, sum(lens))
+    route = torch.full((len(lens), w.n_heads_q), 0 if mode == "all_full" else 1, dtype=torch.uint8)
+    rows = inputs.sampled_rows(w, lens, 256)
+    check_case(q, k, v, lens, route, w.sink, w.window, rows=rows.numpy(), what=f"ragged4 {mode}")
+
+
+def test_long_256k_sampled_rows():
+    w = inputs.WORKLOADS["long_256k"]
+    lens = inputs.lengths(w)
+    q, k, v = inputs.qkv(w, sum(lens))
+    route = inputs.bernoulli_route(w, 1)
+    rows = inputs.sampled_rows(w, lens, w.sampled_rows)
+    check_case(q, k, v, lens, route, w.sink, w.window, rows=rows.numpy(), what=w.name)
+
+
+@pytest.mark.parametrize("kdt", [torch.bfloat16, torch.float32])
+def test_router_ragged_with_empty_sequence(kdt):
+    lens = [300, 0, 1, 77]
+    cu = inputs.cu_seqlens(lens)
+    C, Hh, Hq = 200, 48, 6   # kv_dim not a multiple of 8: the scalar pooling path
+    g = torch.Generator().manual_seed(42)
+    ks = torch.randn(sum(lens), C, generator=g).to(kdt)
+    w1 = torch.randn(Hh, C, generator=g) * 0.3
+    b1 = torch.randn(Hh, generator=g) * 0.1
+    w2 = torch.randn(Hq, Hh, generator=g) * 0.3
+    b2 = torch.randn(Hq, generator=g) * 0.1
+    _, ref_z, ref_r = oracle.route(ks, cu, w1, b1, w2, b2)
+    r = torch.empty(len(lens), Hq, dtype=torch.uint8, device="cuda")
+    z = torch.empty(len(lens), Hq, dtype=torch.float32, device="cuda")
+    ws = H.workspace(len(lens), max(lens), Hq, C, Hh)
+    ea.route(H.to_gpu(ks), H.to_gpu(cu), H.to_gpu(w1), H.to_gpu(b1), H.to_gpu(w2), H.to_gpu(b2),
+             r, ws, logits_out=z)
+    torch.cuda.synchronize()
+    zz = z.cpu().double().numpy()
+    assert np.abs(zz - ref_z).max() < 1e-5
+    # bits must agree wherever the logit is not within float rounding of the threshold
+    decided = np.abs(ref_z) > 1e-5
+    assert np.array_equal(r.cpu().numpy()[decided], ref_r[decided])
