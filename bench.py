@@ -16,6 +16,7 @@ sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,28 @@ from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
 METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
 GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
+ATTN_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_qwen3_8b_32k_traffic.json")
+
+
+def source_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a plain 1 GiB
+    copy), or None if there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != source_sha256(ATTN_SOURCE):
+        return None
+    kib = t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"]
+    return int(round(kib * 1024))
 
 
 def log(msg):
@@ -153,10 +176,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_8b_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one elementwise copy kernel of 1 GiB in and 1 GiB "
+                         "out (a known-size kernel for scaling rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the routed "
@@ -216,9 +243,16 @@ def main():
                          "attention": round(ms_attn, 4)},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128>",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "frac": round(attn_tflops / peak, 4), "traffic": measured_traffic(w.name),
                      "algorithmic_bytes": io, "launch_ms": round(ms_attn, 4)},
     }
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         rec["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
