@@ -18,8 +18,7 @@
 //   * Persistent grid: each workgroup pops items from the longest-first work list with
 //     one atomic per item, so long full-head items start first and short sparse items
 //     fill the tail of the launch.  The last workgroup out re-zeroes the queue.
-//   * Sparse items visit only their sink tiles and window tiles; the element mask is
-//     branch-free and applied only on tiles that are not fully visible for a wavefront.
+//   * Sparse items visit only their sink tiles and window tiles.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers as the B operand,
 //     so each lane owns one query row of S: the row max needs one cross-half exchange
 //     (v_permlane32_swap) and the row sum stays lane-partial until the epilogue.
@@ -32,11 +31,16 @@
 //     per row so the b128 K reads (16 rows) and the transposing V reads (4 rows x 64 bytes
 //     per half-wavefront) hit distinct banks of the 64-bank LDS.
 //   * Softmax uses exp2 with log2(e) folded into the scale; all state is fp32.  P is
-//     taken relative to the new running max (its largest entry is exactly 1); the
-//     O *= alpha pass runs only when some row of the wavefront finds a new maximum.
+//     taken relative to a per-row reference max and rounded to bf16; the row sums add
+//     the rounded values (v_dot2c_f32_bf16).  The reference only has to keep P <= 2^8,
+//     which a row sum <= 2^8 proves, so the row max, the O *= alpha pass and a recompute
+//     of P run only on the (rare) tiles where some lane's sum exceeds that bound.
+//   * Masks are applied only on tiles that hide a pair of the wavefront's rows, in the
+//     cheapest form the tile needs: causal edge only, window edge only, or both.
 //   * Raw buffer loads/stores bound every access: keys past the sequence end read as
 //     zero and rows past the tile end are not stored.
 #include <climits>
+#include <type_traits>
 
 #include "ea_device.h"
 #include "ea_internal.h"
@@ -58,7 +62,7 @@ struct Shape {
   static constexpr int TILE_BYTES = BN * ROW_BYTES;     // one K or V tile
   static constexpr int LDS_BYTES = 4 * TILE_BYTES;      // K and V, double buffered
   static constexpr int ROWS_PER_LOAD = 64 / CHUNKS;     // rows one wave-wide 16-B load fills
-  static constexpr int LOADS = BN / ROWS_PER_LOAD / kWaves;  // per wave per tile, K or V
+  static constexpr int LOADS = BN / ROWS_PER_LOAD / 4;  // per loading wave per tile, K or V
   static constexpr int KSTEPS = D / 16;                 // MFMA k-steps over the head dim
   static constexpr int DT = D / 32;                     // 32-wide output column tiles
   // XOR swizzles of the 16-byte chunk index, per row.  K: chunk ^ (row % CHUNKS) keeps
@@ -87,15 +91,6 @@ __device__ __forceinline__ Visit make_visit(bool sparse, int m0, int m1, int sin
   }
   v.count = v.n1 + max(0, v.t_hi - v.s2 + 1);
   return v;
-}
-
-// True if some (row, key) pair of the tile is hidden for rows [r0, r1).
-__device__ __forceinline__ bool tile_needs_mask(int kt, bool sparse, int r0, int r1, int sink,
-                                                int window) {
-  const int k0 = kt * BN, k1 = k0 + BN;
-  if (k1 - 1 > r0) return true;                       // causal edge (or keys past the end)
-  if (!sparse) return false;
-  return !(k1 <= sink || k0 > r1 - 1 - window);       // neither all-sink nor all-window
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -136,10 +131,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   for (;;) {
     if (tid == 0) s_item = atomicAdd(&a.queue[0], 1);
     __syncthreads();
-    const int it = s_item;
+    // the item index is uniform: keeping it (and so the item, its tile plan and the
+    // buffer offsets) in scalar registers keeps the direct-to-LDS loads' offsets scalar
+    const int it = uniform(s_item);
     if (it >= n_items) break;
     const int4 item = a.items[it];
-    const int b = item.x, h = item.y, qt = item.z;
+    const int b = uniform(item.x), h = uniform(item.y), qt = uniform(item.z);
     // an item outside this call's sizes is skipped (the test is uniform across the
     // workgroup; the barrier keeps s_item stable until every thread has read it)
     if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b]) {
@@ -150,8 +147,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const int len = a.cu[b + 1] - seq0;
     const int m0 = qt * BM, m1 = min(m0 + BM, len);
     const int kvh = h / group;
-    const bool sparse = a.route[(int64_t)b * Hq + h] != 0;
-    const Visit vis = make_visit(sparse, m0, m1, a.sink, a.window);
+    const bool sparse = uniform(a.route[(int64_t)b * Hq + h]) != 0;
+    Visit vis = make_visit(sparse, m0, m1, a.sink, a.window);
+    vis.n1 = uniform(vis.n1);
+    vis.s2 = uniform(vis.s2);
+    vis.t_hi = uniform(vis.t_hi);
+    vis.count = uniform(vis.count);
     const int wr0 = m0 + row0, wr1 = min(wr0 + 32, m1);  // this wavefront's rows
 
     // buffer windows: this item's Q/O rows of head h; this sequence's K/V of head kvh
@@ -164,17 +165,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const auto kr = make_rsrc((const __bf16*)a.k + kv_elem, kv_bytes);
     const auto vr = make_rsrc((const __bf16*)a.v + kv_elem, kv_bytes);
 
-    // Issue the direct-to-LDS loads of one K or V tile into a buffer: each of the 8
-    // wavefronts fills LOADS groups of ROWS_PER_LOAD rows.
+    // Issue the direct-to-LDS loads of one K or V tile into a buffer.  Only the four
+    // wavefronts of group B issue tile loads (in the slots where they run the softmax
+    // phase, which reads no LDS); each fills LOADS groups of ROWS_PER_LOAD rows.
     auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, unsigned char* dst, int kt,
                          bool is_v) {
-      // the wavefront index is uniform; readfirstlane lets the scalar offset stay scalar
-      const int wv = uniform(wave);
+      // the wavefront and tile indices are uniform; readfirstlane keeps the row offset
+      // scalar (the compiler cannot prove it and would otherwise loop over lanes)
+      const int wv = uniform(wave & 3);
+      kt = uniform(kt);
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
         const int lg = wv * S::LOADS + i;
-        const uint32_t row_base = (uint32_t)(kt * BN + lg * S::ROWS_PER_LOAD) * kv_row_bytes;
-        const int r = (wave * S::LOADS + i) * S::ROWS_PER_LOAD + lrow;
+        const uint32_t row_base =
+            (uint32_t)uniform((int)((uint32_t)(kt * BN + lg * S::ROWS_PER_LOAD) * kv_row_bytes));
+        const int r = ((wave & 3) * S::LOADS + i) * S::ROWS_PER_LOAD + lrow;
         const int chunk = pc ^ (is_v ? S::swz_v(r) : S::swz_k(r));
         const uint32_t lane_off = (uint32_t)lrow * kv_row_bytes + (uint32_t)(chunk * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + lg * 1024), 16,
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;  // reference max and lane-partial row sum
     f32x16 sacc[kSubN];   // S(t) from the GEMM phase, consumed by the softmax phase
     bf16x8 pb[kSubN][2];  // P(t) from the softmax phase, consumed by the next GEMM phase
 #pragma unroll
@@ -210,8 +215,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     // MFMAs.  The LDS operands of stage i+1 are read during stage i (sched_barrier keeps
     // the compiler from sinking the reads next to their MFMAs), so one wavefront keeps
     // the matrix core busy on its own while its partner wavefront runs the softmax.
-    auto gemm_phase = [&](int t, int N) {
-      const bool do_pv = t >= 1, do_qk = t < N;
+    // pv / qk: std::true_type or std::false_type (which of the two products to run)
+    auto gemm_phase = [&](int t, auto pv, auto qk) {
+      constexpr bool do_pv = decltype(pv)::value, do_qk = decltype(qk)::value;
       const unsigned char* vb = vbase + ((t - 1) & 1) * S::TILE_BYTES;
       const unsigned char* kb = kbase + (t & 1) * S::TILE_BYTES;
       constexpr int KH = S::KSTEPS / 2;
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
             sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[q], qreg[k0 + q], sacc[j], 0, 0, 0);
         }
       };
-      const int c0 = do_pv ? 0 : 4, c1 = do_qk ? 8 : 4;
+      constexpr int c0 = do_pv ? 0 : 4, c1 = do_qk ? 8 : 4;
       bf16x8 opa[KH], opb[KH];
       read_ops(c0, opa);
       __builtin_amdgcn_sched_barrier(0);
@@ -278,17 +284,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     };
 
-    // Softmax phase Y(t): mask, running max, P(t) = exp2(S*c - m*c) as bf16, row sums,
-    // rescale of O when the max moved.
+    // Softmax phase Y(t).  P(t) = exp2(S*c - m_ref*c) is taken relative to the row's
+    // reference max m_ref, rounded to bf16, and the row sum adds the rounded values
+    // (v_dot2c_f32_bf16 against ones), so numerator and denominator of the output use
+    // the same weights.  A row sum of at most 2^8 bounds every P of the row by 2^8 (P >= 0),
+    // which is all the reference max has to guarantee; only when a lane's sum exceeds it
+    // (or is not finite: no reference yet) does the wavefront take the exact path: row
+    // max, new reference max for every row, O and l rescaled, P recomputed.
+    auto compute_p = [&](float mc) -> float {
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kSubN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r], c_log2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r + 1], c_log2, -mc));
+          const bf16x2 w = {(__bf16)p0, (__bf16)p1};
+          pb[j][r / 8][r % 8] = w[0];
+          pb[j][r / 8][r % 8 + 1] = w[1];
+          ls[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ls[(r / 2) % 4], false);
+        }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
     auto softmax_phase = [&](int t) {
       const int kt = vis.tile(t);
-      if (tile_needs_mask(kt, sparse, wr0, wr1, a.sink, a.window)) {
-        // key kt*BN + off is visible iff off <= qi - kbase and, for a sparse head,
-        // (off >= qi - window + 1 - kbase or off < sink - kbase)
-        const int kbase_key = kt * BN;
-        const int lim = qi - kbase_key;
-        const int wlo = sparse ? qi - a.window + 1 - kbase_key : INT_MIN;
-        const int slim = sparse ? a.sink - kbase_key : INT_MIN;
+      const int k0 = kt * BN;
+      // hidden pairs in this tile for this wavefront's rows: past the diagonal (or past
+      // the sequence end), or below the window start of a sparse row outside the sink
+      const bool m_causal = k0 + BN - 1 > wr0;
+      const bool m_win = sparse && k0 + BN > a.sink && k0 <= wr1 - 1 - a.window;
+      if (m_causal && !m_win) {
+        const int lim = qi - k0;  // key k0 + off is visible iff off <= lim
+#pragma unroll
+        for (int j = 0; j < kSubN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * j + 8 * (r / 4) + 4 * g + (r % 4);
+            sacc[j][r] = off <= lim ? sacc[j][r] : -INFINITY;
+          }
+      } else if (m_win && !m_causal && k0 >= a.sink) {
+        const int wlo = qi - a.window + 1 - k0;  // visible iff off >= wlo
+#pragma unroll
+        for (int j = 0; j < kSubN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 32 * j + 8 * (r / 4) + 4 * g + (r % 4);
+            sacc[j][r] = off >= wlo ? sacc[j][r] : -INFINITY;
+          }
+      } else if (m_causal || m_win) {
+        // general: off <= lim and, for a sparse head, (off >= wlo or off < slim)
+        const int lim = qi - k0;
+        const int wlo = sparse ? qi - a.window + 1 - k0 : INT_MIN;
+        const int slim = sparse ? a.sink - k0 : INT_MIN;
 #pragma unroll
         for (int j = 0; j < kSubN; ++j)
 #pragma unroll
@@ -298,65 +346,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
             sacc[j][r] = visible ? sacc[j][r] : -INFINITY;
           }
       }
-      // row max and row sum as 8-way trees (short dependency chains)
-      float mx[8];
+      float lt = compute_p(m_ref * c_log2);
+      if (__builtin_amdgcn_ballot_w64(!(lt <= 256.f)) != 0) {
+        // row max as a tree of 3-input maxima, then across the two lanes of the row
+        float mx[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) mx[i] = fmaxf(sacc[i / 4][4 * (i % 4)], sacc[i / 4][4 * (i % 4) + 1]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        mx[i] = fmaxf(mx[i], fmaxf(sacc[i / 4][4 * (i % 4) + 2], sacc[i / 4][4 * (i % 4) + 3]));
-      float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
-                       fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
-      mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float mc = (m_new == -INFINITY ? 0.f : m_new) * c_log2;
-      float ps[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ps[i] = 0.f;
-#pragma unroll
-      for (int j = 0; j < kSubN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r], c_log2, -mc));
-          ps[(16 * j + r) % 8] += p;
-          pb[j][r / 8][r % 8] = (__bf16)p;
+        for (int i = 0; i < 8; ++i) {
+          const int j = i / 4, r = 4 * (i % 4);
+          mx[i] = fmaxf(fmaxf(sacc[j][r], sacc[j][r + 1]), fmaxf(sacc[j][r + 2], sacc[j][r + 3]));
         }
-      const float psum = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-      // rescale O and l when some row of the wavefront has a new max (alpha = 1 elsewhere)
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
+                         fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+        mt = fmaxf(mt, xor32(mt));
+        const float m_new = fmaxf(m_ref, mt);
+        // alpha = 0 when there was no reference yet (O and l are still zero)
         const float alpha =
-            m_new == m_run ? 1.0f : __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+            m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c_log2);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        m_ref = m_new;
+        lt = compute_p((m_ref == -INFINITY ? 0.f : m_ref) * c_log2);
       }
-      l_run += psum;
-      m_run = m_new;
+      l_run += lt;
     };
 
     // Slot schedule.  Tiles t = 0..N-1.  Group A runs X(t) in slot 2t and Y(t) in slot
     // 2t+1; group B runs Y(t-1) in slot 2t and X(t) in slot 2t+1; X(N) is the last P V.
-    // K(t) is read in slots 2t, 2t+1 and V(t) in slots 2t+2, 2t+3; both are loaded at the
-    // start of slot 2t-2 (K) / 2t (V) into the buffer freed two slots earlier, and every
-    // odd slot ends with a full wait, so each load has two slots to land.
-    const int N = vis.count;
-    load_tile(kr, kbase, vis.tile(0), false);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int s = 0; s < 2 * N + 2; ++s) {
-      const int u = s >> 1;
-      if ((s & 1) == 0) {
+    // K(t) is read in slots 2t, 2t+1 and V(t) in slots 2t+2, 2t+3; group B loads both at
+    // the start of slot 2t-2 (K) / 2t (V), while it runs a softmax phase, into the buffer
+    // freed by the barrier before.  Group B's next GEMM phase, one slot later, is the first
+    // LDS read after its loads (the compiler waits for them there: the DMA writes may alias
+    // any LDS read), and every odd slot ends with a full wait, so a load never stalls the
+    // GEMM phase of the slot that issued it.
+    const int N = vis.count;  // >= 1 for every valid item
+    const std::true_type yes;
+    const std::false_type no;
+    // group B issues K(u+1) and V(u) at the start of slot 2u
+    auto issue_loads = [&](int u) {
+      if (grp == 1) {
         if (u + 1 < N) load_tile(kr, kbase + ((u + 1) & 1) * S::TILE_BYTES, vis.tile(u + 1), false);
-        if (u < N) load_tile(vr, vbase + (u & 1) * S::TILE_BYTES, vis.tile(u), true);
+        load_tile(vr, vbase + (u & 1) * S::TILE_BYTES, vis.tile(u), true);
       }
-      if ((s & 1) == grp) {
-        gemm_phase(u, N);
-      } else {
-        const int ty = grp == 0 ? u : u - 1;
-        if (ty >= 0 && ty < N) softmax_phase(ty);
-      }
+    };
+    auto slot_end = [&](int s) {
       if (s & 1) {
         __builtin_amdgcn_s_waitcnt(0);  // this slot's LDS reads and the loads of slot s-1
         __syncthreads();
@@ -364,6 +399,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads of this slot are done
         __builtin_amdgcn_s_barrier();
       }
+    };
+    if (grp == 1) load_tile(kr, kbase, vis.tile(0), false);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // slots 0, 1: S(0) only (A then B); A runs Y(0) in slot 1
+    for (int s = 0; s < 2; ++s) {
+      if (s == 0) issue_loads(0);
+      if ((s & 1) == grp)
+        gemm_phase(0, no, yes);
+      else if (s == 1)
+        softmax_phase(0);
+      slot_end(s);
+    }
+    // steady state: slots 2 .. 2N-1, every GEMM phase runs P V and Q K^T
+    for (int s = 2; s < 2 * N; ++s) {
+      const int u = s >> 1;
+      if ((s & 1) == 0) issue_loads(u);
+      if ((s & 1) == grp)
+        gemm_phase(u, yes, yes);
+      else
+        softmax_phase(grp == 0 ? u : u - 1);
+      slot_end(s);
+    }
+    // slots 2N, 2N+1: the last P V (A then B); B runs Y(N-1) in slot 2N
+    for (int s = 2 * N; s < 2 * N + 2; ++s) {
+      if ((s & 1) == grp)
+        gemm_phase(N, yes, no);
+      else if ((s & 1) == 0)
+        softmax_phase(N - 1);
+      slot_end(s);
     }
 
     // ---- epilogue: O = O / l, round to bf16, store this lane's query row
@@ -381,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         buf_store8(orr, row_off + d0 * 2, w);
       }
     if (a.lse && g == 0 && qi < m1) {
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       a.lse[(int64_t)h * total_tokens + seq0 + qi] = m_use * a.scale + logf(l_tot);
     }
     __syncthreads();  // s_item and the LDS tiles are reused by the next item

@@ -46,7 +46,10 @@ def check_case(q, k, v, lens, route, sink, window, rows=None, what="", guard=0, 
     ro, rlse = oracle.attn(q, k, v, cu, hq, hkv, route.numpy(), sink, window, rows=rows)
     sel = slice(None) if rows is None else torch.as_tensor(rows)
     H.compare(o[sel], ro, q.dtype, what, strict=strict)
-    tol = 1e-3 if q.dtype == torch.bfloat16 else 1e-5
+    # bf16: the row sum adds the bf16-rounded weights P (each within the unit roundoff
+    # 2^-8 relative of the exact value), so ln(l) is within ln(1 + 2^-8) < 3.9e-3 of the
+    # exact log-sum-exp, plus fp32 accumulation of the scores.  fp32: 1e-5.
+    tol = 4e-3 if q.dtype == torch.bfloat16 else 1e-5
     lse_sel = lse[:, sel].T.double().numpy()
     assert np.abs(lse_sel - rlse).max() <= tol, what
     ref_items = oracle_worklist(route, lens, hq, sink, window, ea.dtype_code(q.dtype), q.shape[2])
