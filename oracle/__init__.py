@@ -12,6 +12,7 @@ and the readings taken where the pages are silent.
 
 Functions:
   attn(...)      masked-softmax attention over explicit per-head visible sets
+  decode(...)    one decode step of the same attention over a per-sequence KV cache
   route(...)     mean-pool -> MLP (SiLU) -> logits -> hard threshold
   worklist(...)  (seq, head, q_tile, cost) items, longest first
   build()        compile the C oracle (gcc -O2 -fopenmp)
@@ -55,6 +56,9 @@ def _load():
         lib.oracle_attn.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, P, i32, i32, dbl,
                                     P, i64, P, P, i32]
         lib.oracle_attn.restype = i32
+        lib.oracle_decode.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
+                                      dbl, P, P, i32]
+        lib.oracle_decode.restype = i32
         lib.oracle_route.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P]
         lib.oracle_route.restype = i32
         lib.oracle_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i64,
@@ -135,6 +139,34 @@ def attn(q, k, v, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window, scale=
                          o.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_attn failed with code {rc}")
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, n_heads_kv, route, sink, window, scale=None,
+           nthreads=0):
+    """fp64 decode step.  q [B, Hq, D], k_cache/v_cache [B, cap, Hkv, D] (one dtype),
+    seqlens [B] (tokens in each cache, the newest being the query's own), route [B, Hq].
+    Returns (o [B, Hq, D] float64, lse [B, Hq] float64)."""
+    lib = _load()
+    qa, dt = _as_elements(q)
+    ka, dtk = _as_elements(k_cache)
+    va, dtv = _as_elements(v_cache)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k_cache, v_cache must share one dtype")
+    batch, hq, d = (int(x) for x in qa.shape)
+    cap = int(ka.shape[1])
+    sl = _np(seqlens, np.int32).reshape(batch)
+    r = _np(route, np.uint8).reshape(batch, hq)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((batch, hq, d), dtype=np.float64)
+    lse = np.empty((batch, hq), dtype=np.float64)
+    rc = lib.oracle_decode(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt, sl.ctypes.data,
+                           batch, cap, hq, int(n_heads_kv), d, r.ctypes.data, int(sink),
+                           int(window), float(scale), o.ctypes.data, lse.ctypes.data,
+                           int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed with code {rc}")
     return o, lse
 
 

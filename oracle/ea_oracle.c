@@ -150,6 +150,70 @@ int oracle_attn(const void* q, const void* k, const void* v, int dtype,
 }
 
 /*
+ * One decode step of the same routed attention: sequence b holds seqlens[b] tokens in its
+ * cache (the newest one, at position i = seqlens[b] - 1, is the query's own token), and
+ * each query head attends from position i under its mode exactly as a prefill row at
+ * position i would [Blog §2.1 modes; the sparse pattern as above].  Layouts: q/o
+ * [batch, hq, d]; k_cache/v_cache [batch, cap, hkv, d]; seqlens [batch] with
+ * 1 <= seqlens[b] <= cap.  lse_out [batch, hq] (nullable).
+ */
+int oracle_decode(const void* q, const void* kc, const void* vc, int dtype,
+                  const int32_t* seqlens, int batch, int cap, int hq, int hkv, int d,
+                  const uint8_t* route, int sink, int window, double scale,
+                  double* o_out, double* lse_out, int nthreads) {
+  if (batch < 1 || cap < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 || window < 1 ||
+      sink < 0)
+    return -1;
+  for (int b = 0; b < batch; ++b)
+    if (seqlens[b] < 1 || seqlens[b] > cap) return -1;
+  const int group = hq / hkv;
+  const int64_t n_tasks = (int64_t)batch * hq;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel reduction(| : bad)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!x || !acc) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < n_tasks; ++task) {
+      if (!x || !acc) continue;
+      const int b = (int)(task / hq);
+      const int h = (int)(task % hq);
+      const int g = h / group;
+      const int64_t i = seqlens[b] - 1;
+      const int sparse = route[task] != 0;
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= i; ++j) {
+        if (!key_visible(i, j, sparse, sink, window)) continue;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e)
+          dot += elem(q, dtype, task * d + e) *
+                 elem(kc, dtype, (((int64_t)b * cap + j) * hkv + g) * d + e);
+        x[j] = scale * dot;
+        if (x[j] > m) m = x[j];
+      }
+      double sum = 0.0;
+      for (int e = 0; e < d; ++e) acc[e] = 0.0;
+      for (int64_t j = 0; j <= i; ++j) {
+        if (!key_visible(i, j, sparse, sink, window)) continue;
+        const double p = exp(x[j] - m);
+        sum += p;
+        for (int e = 0; e < d; ++e)
+          acc[e] += p * elem(vc, dtype, (((int64_t)b * cap + j) * hkv + g) * d + e);
+      }
+      for (int e = 0; e < d; ++e) o_out[task * d + e] = acc[e] / sum;
+      if (lse_out) lse_out[task] = m + log(sum);
+    }
+    free(x);
+    free(acc);
+  }
+  return bad ? -2 : 0;
+}
+
+/*
  * Attention Router [Blog §2.1]: reads the key hidden states of each sequence and emits
  * one routing signal per query head.  x = mean over the sequence's tokens of
  * ks[t, :] (an empty sequence gives x = 0); u = W1 x + b1; h = u * sigmoid(u) (SiLU);

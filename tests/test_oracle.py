@@ -353,3 +353,98 @@ def test_visible_pair_closed_form(L, sink, window):
     for sparse in (False, True):
         assert metrics.visible_pairs(L, sparse, sink, window) == int(
             lib_mask(L, sparse, sink, window).sum())
+
+
+# ---- decode step (one new query per sequence over its KV cache) ----
+
+def make_cache(lens, cap, hq, hkv, d, seed, poison=True):
+    """Per-sequence caches [B, cap, Hkv, D] with the slots past each length filled with NaN
+    (they must never be read), plus the query of each sequence's newest token."""
+    g = np.random.default_rng(seed)
+    B = len(lens)
+    kc = g.standard_normal((B, cap, hkv, d))
+    vc = g.standard_normal((B, cap, hkv, d))
+    if poison:
+        for b, L in enumerate(lens):
+            kc[b, L:] = np.nan
+            vc[b, L:] = np.nan
+    q = g.standard_normal((B, hq, d))
+    return q, kc, vc
+
+
+@pytest.mark.parametrize("L,sink,window", [(1, 0, 1), (2, 1, 1), (7, 2, 3), (9, 0, 4),
+                                           (12, 4, 20), (10, 12, 2), (13, 3, 13)])
+def test_decode_tiny_bruteforce(L, sink, window):
+    """The decode output of a cache holding L tokens is the last row of the brute-force
+    prefill of those L tokens (pair-loop mask, dense softmax)."""
+    d, hq, hkv, cap = 5, 4, 2, L + 3
+    q, kc, vc = make_cache([L], cap, hq, hkv, d, seed=L * 31 + sink)
+    route = [[1, 0, 0, 1]]
+    scale = 0.41
+    o, lse = oracle.decode(q, kc, vc, [L], hkv, route, sink, window, scale)
+    for h in range(hq):
+        kk, vv = kc[0, :L, h // 2], vc[0, :L, h // 2]
+        qq = np.zeros((L, d))
+        qq[L - 1] = q[0, h]
+        ref = dense_bruteforce(qq, kk, vv, L, route[0][h], sink, window, scale)[L - 1]
+        np.testing.assert_allclose(o[0, h], ref, atol=1e-12, rtol=0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_decode_matches_sdpa_last_row_ragged_gqa():
+    """Library routine: torch SDPA (fp64) of the whole sequence under the library-built
+    mask, last row, for a ragged batch with GQA 4:1 and mixed routing."""
+    lens, cap, hq, hkv, d = [1, 37, 130, 64, 200], 211, 8, 2, 16
+    q, kc, vc = make_cache(lens, cap, hq, hkv, d, seed=77)
+    route = np.array([[(b + h) % 3 == 0 for h in range(hq)] for b in range(len(lens))],
+                     dtype=np.uint8)
+    sink, window, scale = 5, 40, 0.23
+    o, lse = oracle.decode(q, kc, vc, lens, hkv, route, sink, window, scale)
+    G = hq // hkv
+    for b, L in enumerate(lens):
+        for h in range(hq):
+            m = lib_mask(L, bool(route[b, h]), sink, window)[L - 1:L]
+            qq = torch.as_tensor(q[b, h][None], dtype=torch.float64)
+            kk = torch.as_tensor(kc[b, :L, h // G], dtype=torch.float64)
+            vv = torch.as_tensor(vc[b, :L, h // G], dtype=torch.float64)
+            ref = F.scaled_dot_product_attention(qq[None], kk[None], vv[None],
+                                                 attn_mask=m[None], scale=scale)[0, 0]
+            np.testing.assert_allclose(o[b, h], ref.numpy(), atol=1e-12, rtol=0)
+            sc = (qq @ kk.T * scale).masked_fill(~m, -math.inf).numpy()
+            assert abs(lse[b, h] - logsumexp(sc[0])) < 1e-12
+
+
+def test_decode_special_cases():
+    d, hq, hkv, cap = 6, 2, 1, 20
+    # one cached token: the output is that token's value, lse = scale * q.k0
+    q, kc, vc = make_cache([1], cap, hq, hkv, d, seed=5)
+    o, lse = oracle.decode(q, kc, vc, [1], hkv, [[0, 1]], 0, 1, 0.5)
+    for h in range(hq):
+        np.testing.assert_array_equal(o[0, h], vc[0, 0, 0])
+        assert abs(lse[0, h] - 0.5 * float(q[0, h] @ kc[0, 0, 0])) < 1e-12
+    # a window (or sink) covering the cache makes a sparse head equal to a full head
+    q, kc, vc = make_cache([17], cap, hq, hkv, d, seed=6)
+    full, _ = oracle.decode(q, kc, vc, [17], hkv, [[0, 0]], 0, 1, 0.3)
+    for sink, window in [(0, 17), (17, 1), (3, 40)]:
+        sp, _ = oracle.decode(q, kc, vc, [17], hkv, [[1, 1]], sink, window, 0.3)
+        np.testing.assert_array_equal(sp, full)
+    # constant values give that constant whatever the scores
+    vc2 = np.where(np.isnan(vc), np.nan, 2.5)
+    o, _ = oracle.decode(q, kc, vc2, [17], hkv, [[0, 1]], 2, 5, 0.3)
+    np.testing.assert_allclose(o, 2.5, atol=1e-14, rtol=0)
+    # sink 1, window 1: exactly key 0 and the newest key
+    o, _ = oracle.decode(q, kc, vc, [17], hkv, [[1, 1]], 1, 1, 0.3)
+    for h in range(hq):
+        x0, x1 = 0.3 * q[0, h] @ kc[0, 0, 0], 0.3 * q[0, h] @ kc[0, 16, 0]
+        w0 = 1.0 / (1.0 + math.exp(x1 - x0))
+        np.testing.assert_allclose(o[0, h], w0 * vc[0, 0, 0] + (1 - w0) * vc[0, 16, 0],
+                                   atol=1e-12, rtol=0)
+
+
+def test_decode_rejects_bad_arguments():
+    q, kc, vc = make_cache([3], 4, 2, 1, 4, seed=9, poison=False)
+    for lens in ([0], [5]):
+        with pytest.raises(ValueError):
+            oracle.decode(q, kc, vc, lens, 1, [[0, 0]], 0, 2)
+    with pytest.raises(ValueError):
+        oracle.decode(q, kc, vc, [3], 1, [[0, 0]], 0, 0)
