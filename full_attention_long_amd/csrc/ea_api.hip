@@ -374,4 +374,81 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
                       worklist_capacity, counters + 1, grid_blocks, (hipStream_t)stream);
 }
 
+size_t ea_decode_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q,
+                                int32_t head_dim) {
+  if (batch < 1 || max_seqlen < 1 || n_heads_q < 1 || head_dim < 1) return 0;
+  const int64_t splits = ceil_div64(max_seqlen, kDecodeSplit);
+  const int64_t slots = (int64_t)batch * n_heads_q * splits;
+  if (slots > ((int64_t)1 << 40) / (head_dim + 2)) return 0;
+  return align256((size_t)slots * head_dim * 4) + align256((size_t)slots * 2 * 4);
+}
+
+ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                void* o, ea_dtype dt, const int32_t* seqlens,
+                                const int32_t* seqlens_host, int32_t batch,
+                                int32_t cache_capacity, int32_t max_seqlen, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                                int32_t sink, int32_t window, float scale, float* lse_out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k_cache || !v_cache || !o || !seqlens || !route || !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || cache_capacity < 1 || max_seqlen < 1)
+    return fail(EA_ERR_INVALID_ARG, "need batch >= 1, cache_capacity >= 1, max_seqlen >= 1");
+  if (max_seqlen > cache_capacity) return fail(EA_ERR_INVALID_ARG, "max_seqlen > cache_capacity");
+  if (n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(EA_ERR_INVALID_ARG, "n_heads_q must be a positive multiple of n_heads_kv");
+  if (n_heads_q / n_heads_kv > kDecodeMaxGroup)
+    return fail(EA_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (head_dim != 64 && head_dim != 128) return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  if (isnan(scale) || isinf(scale)) return fail(EA_ERR_INVALID_ARG, "scale is not finite");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(EA_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const int64_t elem = dt == EA_BF16 ? 2 : 4;
+  // each sequence's KV-head window of the cache uses 32-bit byte offsets
+  if ((int64_t)cache_capacity * n_heads_kv * head_dim * elem >= ((int64_t)1 << 31))
+    return fail(EA_ERR_UNSUPPORTED, "cache too long for 32-bit per-sequence addressing");
+  const size_t qo_bytes = (size_t)batch * n_heads_q * head_dim * elem;
+  const size_t cache_bytes = (size_t)batch * cache_capacity * n_heads_kv * head_dim * elem;
+  if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(o, qo_bytes, k_cache, cache_bytes) ||
+      overlaps(o, qo_bytes, v_cache, cache_bytes))
+    return fail(EA_ERR_INVALID_ARG, "o overlaps q or a cache");
+  if (seqlens_host)
+    for (int32_t b = 0; b < batch; ++b)
+      if (seqlens_host[b] < 1 || seqlens_host[b] > max_seqlen)
+        return fail(EA_ERR_INVALID_ARG, "seqlens must lie in [1, max_seqlen]");
+  const size_t need = ea_decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim);
+  if (need == 0) return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < need) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_decode_workspace_size()");
+  const int64_t splits = ceil_div64(max_seqlen, kDecodeSplit);
+  if (splits > 2147483647 / 2) return fail(EA_ERR_UNSUPPORTED, "too many splits");
+  DecodeArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.o = o;
+  a.seqlens = seqlens;
+  a.route = route;
+  a.o_part = (float*)workspace;
+  a.ml_part = (float*)((char*)workspace +
+                       align256((size_t)batch * n_heads_q * splits * head_dim * 4));
+  a.lse = lse_out;
+  a.batch = batch;
+  a.cap = cache_capacity;
+  a.max_seqlen = max_seqlen;
+  a.max_splits = (int)splits;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+  const hipError_t e = launch_decode(a, dt == EA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return EA_OK;
+}
+
 }  // extern "C"

@@ -75,6 +75,25 @@ struct AttnArgs {
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int grid, hipStream_t stream);
+// One decode step (ea_decode.hip): per-split partial results in the workspace, then a
+// combine.  kDecodeSplit keys per split; group sizes up to kDecodeMaxGroup.
+constexpr int kDecodeSplit = 256;
+constexpr int kDecodeMaxGroup = 8;
+struct DecodeArgs {
+  const void* q;          // [batch, n_heads_q, head_dim]
+  const void* kc;         // [batch, cap, n_heads_kv, head_dim]
+  const void* vc;
+  void* o;                // [batch, n_heads_q, head_dim]
+  const int32_t* seqlens; // [batch]
+  const uint8_t* route;   // [batch, n_heads_q]
+  float* o_part;          // [batch, n_heads_q, max_splits, head_dim]
+  float* ml_part;         // [batch, n_heads_q, max_splits, 2]: split max (log2 units), sum
+  float* lse;             // [batch, n_heads_q] or null
+  int batch, cap, max_seqlen, max_splits, n_heads_q, n_heads_kv, head_dim, sink, window;
+  float scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+
 // Workgroups of each attention kernel that fit on one CU at once.
 int attn_bf16_blocks_per_cu();
 int attn_f32_blocks_per_cu();

@@ -18,7 +18,8 @@ EA_OK, EA_ERR_INVALID_ARG, EA_ERR_UNSUPPORTED, EA_ERR_WORKSPACE, EA_ERR_HIP = ra
 EA_BF16, EA_F32 = 0, 1
 
 EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_error",
-           "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run")
+           "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run",
+           "ea_decode_workspace_size", "ea_hybrid_attn_decode")
 
 _lib = None
 
@@ -59,6 +60,11 @@ def lib():
     L.ea_hybrid_attn_run.argtypes = [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
                                      f32, P, P, i64, P, i32, P, sz, P]
     L.ea_hybrid_attn_run.restype = i32
+    L.ea_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.ea_decode_workspace_size.restype = sz
+    L.ea_hybrid_attn_decode.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, P,
+                                        i32, i32, f32, P, P, sz, P]
+    L.ea_hybrid_attn_decode.restype = i32
     _lib = L
     return L
 
@@ -176,3 +182,24 @@ def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window
                                     int(grid_blocks), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)))
+
+
+def decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim) -> int:
+    return int(lib().ea_decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim))
+
+
+def hybrid_attn_decode(q, k_cache, v_cache, o, seqlens, max_seqlen, route_bits, sink, window,
+                       workspace, scale=0.0, seqlens_host=None, lse_out=None, stream=None):
+    """ea_hybrid_attn_decode: q/o [B, Hq, D], k_cache/v_cache [B, cap, Hkv, D] (bf16 or fp32),
+    seqlens [B] int32 device."""
+    batch = q.shape[0]
+    host = None
+    if seqlens_host is not None:
+        host = (ctypes.c_int32 * batch)(*[int(x) for x in seqlens_host])
+    _check(lib().ea_hybrid_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                       dtype_code(q.dtype), _ptr(seqlens), host, batch,
+                                       k_cache.shape[1], max_seqlen, q.shape[1], k_cache.shape[2],
+                                       q.shape[2], _ptr(route_bits), sink, window, float(scale),
+                                       _ptr(lse_out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))

@@ -20,6 +20,7 @@ import torch
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_KS, STREAM_W1, STREAM_W2 = 0, 1, 2, 3, 4, 5
 STREAM_ROUTE, STREAM_LENS, STREAM_ROWS = 6, 7, 8
+STREAM_DEC_Q, STREAM_DEC_K, STREAM_DEC_V, STREAM_DEC_LENS = 9, 10, 11, 12
 
 
 def seed(workload: int, stream: int) -> int:
@@ -156,3 +157,59 @@ def sampled_rows(w: Workload, lens, per_seq: int, bm: int = 128) -> torch.Tensor
         out.extend(start + x for x in pick)
         start += n
     return torch.tensor(out, dtype=torch.int64)
+
+
+# ---- decode steps: one new query per sequence over a per-sequence KV cache
+@dataclass(frozen=True)
+class DecodeWorkload:
+    index: int                      # k in the seed scheme (distinct from the prefill ones)
+    name: str
+    dtype: torch.dtype
+    batch: int
+    capacity: int                   # cache slots per sequence
+    n_heads_q: int
+    n_heads_kv: int
+    head_dim: int
+    sink: int
+    window: int
+    p_sparse: float
+    lengths: tuple = ()             # fixed lengths; empty -> U[len_range] per sequence
+    len_range: tuple = (1, 1)
+
+
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload(11, "decode_tiny_fp32", torch.float32, 3, 320, 4, 2, 64, 16, 64, 0.5,
+                       lengths=(1, 70, 300)),
+        DecodeWorkload(12, "decode_llama8b_8k", torch.bfloat16, 4, 8192, 32, 8, 128, 128, 1024,
+                       0.7, lengths=(8192,) * 4),
+        DecodeWorkload(13, "decode_qwen3_8b_32k", torch.bfloat16, 16, 32768, 32, 8, 128, 128,
+                       2048, 0.85, lengths=(32768,) * 16),
+        DecodeWorkload(14, "decode_ragged", torch.bfloat16, 8, 32768, 32, 8, 128, 64, 1024, 0.68,
+                       len_range=(1, 32768)),
+        DecodeWorkload(15, "decode_long_256k", torch.bfloat16, 1, 262144, 32, 8, 128, 128, 4096,
+                       0.8, lengths=(262144,)),
+    ]
+}
+
+
+def decode_lengths(w: DecodeWorkload) -> list:
+    if w.lengths:
+        return list(w.lengths)
+    g = gen(w.index, STREAM_DEC_LENS)
+    lo, hi = w.len_range
+    return [int(x) for x in torch.randint(lo, hi + 1, (w.batch,), generator=g)]
+
+
+def decode_inputs(w: DecodeWorkload, batch: int = 0):
+    """q [B, Hq, D] and caches [B, cap, Hkv, D] (N(0,1) in w.dtype) for the first `batch`
+    sequences (0 = all), plus their lengths and Bernoulli(p_sparse) routing [B, Hq]."""
+    B = batch or w.batch
+    lens = decode_lengths(w)[:B]
+    q = normal((B, w.n_heads_q, w.head_dim), w.index, STREAM_DEC_Q, w.dtype)
+    kc = normal((B * w.capacity, w.n_heads_kv, w.head_dim), w.index, STREAM_DEC_K, w.dtype)
+    vc = normal((B * w.capacity, w.n_heads_kv, w.head_dim), w.index, STREAM_DEC_V, w.dtype)
+    shape = (B, w.capacity, w.n_heads_kv, w.head_dim)
+    g = gen(w.index, STREAM_ROUTE)
+    route = (torch.rand(w.batch, w.n_heads_q, generator=g) < w.p_sparse).to(torch.uint8)[:B]
+    return q, kc.view(shape), vc.view(shape), lens, route

@@ -171,6 +171,48 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
                              int32_t grid_blocks, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/*
+ * Bytes of workspace ea_hybrid_attn_decode needs for these sizes: per-split partial
+ * results, batch * n_heads_q * ceil(max_seqlen / 256) * (head_dim + 2) floats.
+ * batch >= 1, max_seqlen >= 1, n_heads_q >= 1, head_dim >= 1; 0 if the sizes overflow.
+ */
+size_t ea_decode_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q,
+                                int32_t head_dim);
+
+/*
+ * One decode step of the routed hybrid attention (blog post section 2.1: r = 0 runs Full
+ * Attention, r = 1 Sparse Attention; sparse pattern as above).  Sequence b holds
+ * L = seqlens[b] tokens in its KV cache, the newest being the query's own token, and every
+ * query head attends from position i = L - 1 exactly as a prefill row at position i:
+ *   visible = { j < L }                                   if route[b, h] == 0
+ *           = { j < L : j < sink or j > i - window }       otherwise
+ *   o = sum_{j in visible} softmax_j(scale * <q, k_j>) v_j   -> O[b, h, :]
+ *   lse = log sum_{j in visible} exp(scale * <q, k_j>)      -> lse_out[b, h]
+ * q, o         [batch, n_heads_q, head_dim], dtype dt (EA_BF16 or EA_F32; fp32
+ *              arithmetic, O rounded once to dt)
+ * k_cache, v_cache  [batch, cache_capacity, n_heads_kv, head_dim], dtype dt; only the
+ *              first seqlens[b] slots of sequence b are read (and of them, for a KV head
+ *              whose query heads are all sparse, only the visible ones)
+ * seqlens      [batch] int32 device; each must lie in [1, min(cache_capacity, max_seqlen)]
+ *              (a sequence outside that range gets NaN outputs and no cache reads beyond
+ *              its slots).  seqlens_host: nullable host copy that enables the host check.
+ * head_dim 64 or 128; n_heads_q % n_heads_kv == 0 with at most 8 query heads per KV head;
+ * sink >= 0; window >= 1; scale <= 0 selects 1/sqrt(head_dim)
+ * route        [batch, n_heads_q] uint8 (0 full, nonzero sparse)
+ * lse_out      nullable, [batch, n_heads_q] fp32
+ * workspace    at least ea_decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim)
+ *              bytes, 256-byte aligned; o must not overlap q or the caches
+ * Two launches: per (KV-cache split of 256 keys, KV head, sequence) partial results, then
+ * their combination; results do not depend on scheduling.
+ */
+ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                void* o, ea_dtype dt, const int32_t* seqlens,
+                                const int32_t* seqlens_host, int32_t batch,
+                                int32_t cache_capacity, int32_t max_seqlen, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                                int32_t sink, int32_t window, float scale, float* lse_out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,51 @@ def test_valid_call_without_gpu_reports_hip_error():
     # every check passes, so the first HIP call runs and fails: the status is EA_ERR_HIP
     assert prefill() == ea.EA_ERR_HIP
     assert "device" in ea.last_error() or "launch" in ea.last_error()
+
+
+def decode_call(**kw):
+    args = dict(q=FAKE, kc=FAKE + 0x100000, vc=FAKE + 0x200000, o=FAKE + 0x10000,
+                dt=ea.EA_BF16, seqlens=FAKE, seqlens_host=None, batch=2, cap=4096,
+                max_seqlen=4096, hq=32, hkv=8, d=128, route=FAKE, sink=128, window=1024,
+                scale=0.0, lse=None, ws=0x40000000, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return ea.lib().ea_hybrid_attn_decode(*args.values())
+
+
+def test_decode_workspace_size():
+    a = ea.decode_workspace_size(1, 32768, 32, 128)
+    assert a >= 32 * 128 * (128 + 2) * 4  # 128 splits of 256 keys
+    assert ea.decode_workspace_size(2, 32768, 32, 128) > a
+    assert ea.decode_workspace_size(0, 10, 1, 128) == 0
+    assert ea.decode_workspace_size(1, 0, 1, 128) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.EA_ERR_INVALID_ARG),
+    (dict(seqlens=None), ea.EA_ERR_INVALID_ARG),
+    (dict(ws=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dt=5), ea.EA_ERR_INVALID_ARG),
+    (dict(batch=0), ea.EA_ERR_INVALID_ARG),
+    (dict(max_seqlen=5000), ea.EA_ERR_INVALID_ARG),       # beyond the cache capacity
+    (dict(hq=30), ea.EA_ERR_INVALID_ARG),                 # not a multiple of hkv
+    (dict(hq=72), ea.EA_ERR_UNSUPPORTED),                 # 9 query heads per KV head
+    (dict(d=96), ea.EA_ERR_UNSUPPORTED),
+    (dict(window=0), ea.EA_ERR_INVALID_ARG),
+    (dict(sink=-1), ea.EA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ea.EA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), ea.EA_ERR_INVALID_ARG),            # misaligned
+    (dict(ws=0x40000010), ea.EA_ERR_INVALID_ARG),         # workspace not 256-byte aligned
+    (dict(o=FAKE + 0x100000), ea.EA_ERR_INVALID_ARG),     # o overlaps the K cache
+    (dict(ws_bytes=1024), ea.EA_ERR_WORKSPACE),
+    (dict(cap=1 << 20, max_seqlen=1 << 20), ea.EA_ERR_UNSUPPORTED),  # 32-bit offsets
+])
+def test_decode_rejects(kw, status):
+    assert decode_call(**kw) == status
+    assert ea.last_error()
+
+
+def test_decode_host_seqlens_checks():
+    bad = (ctypes.c_int32 * 2)(0, 17)
+    assert decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
+    bad = (ctypes.c_int32 * 2)(4097, 17)
+    assert decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
