@@ -12,6 +12,12 @@ each), ms per layer, % of the bf16 dense MFMA peak, the roofline of the attentio
 sample of the same workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds S]
+
+With --mode decode it instead times one decode step of the same routed attention
+(ea_hybrid_attn_decode: every sequence's newest token against its KV cache) on 16 sequences
+of 32K cached tokens, priced against HBM bandwidth: the bytes are the K and V cache rows each
+KV-head group must see (all rows if any of its query heads is full, else sink and window),
+plus q and o.
 """
 from __future__ import annotations
 
@@ -30,9 +36,12 @@ sys.path.insert(0, ROOT)
 from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
 METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
+DECODE_METRIC = "hybrid-attn decode step: cache GB/s (% HBM peak), 16 x 32K"
 GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
 ATTN_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_qwen3_8b_32k_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_decode.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_qwen3_8b_32k_traffic.json")
 
 
 def source_sha256(path):
@@ -40,16 +49,16 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a plain 1 GiB
-    copy), or None if there is none for this workload or the kernel source changed
-    since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload, traffic_file=TRAFFIC_FILE, source=ATTN_SOURCE):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a plain 1 GiB copy), or None
+    if there is none for this workload or the kernel source changed since the counters
+    were taken."""
+    if not os.path.exists(traffic_file):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(traffic_file) as f:
         t = json.load(f)
-    if t.get("workload") != workload or t.get("kernel_source_sha256") != source_sha256(ATTN_SOURCE):
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != source_sha256(source):
         return None
     kib = t["fetch_kib_per_dispatch"] * t["fetch_scale"] + t["write_kib_per_dispatch"] * t["write_scale"]
     return int(round(kib * 1024))
@@ -123,6 +132,17 @@ class Layer:
         return metrics.effective_flops(self.lens, r, self.w.head_dim, self.w.sink, self.w.window)
 
 
+def copy_calibration():
+    """One elementwise kernel that reads 1 GiB and writes 1 GiB: a known-size launch for
+    scaling rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def time_events(fn, n):
     """Average ms of fn() over n calls, HIP events on the current (launch) stream."""
     s = torch.cuda.Event(enable_timing=True)
@@ -172,12 +192,116 @@ def cpu_baseline(layer: Layer, seconds: float):
                       f"extrapolated to {full_layer_s:.0f} s"}
 
 
+class DecodeStep:
+    """Resident device buffers of one synthetic decode step."""
+
+    def __init__(self, name: str):
+        w = inputs.DECODE_WORKLOADS[name]
+        self.w = w
+        q, kc, vc, lens, route = inputs.decode_inputs(w)
+        self.cpu = (q, kc, vc, route)
+        self.lens = lens
+        dev = torch.device("cuda:0")
+        self.q, self.kc, self.vc = q.to(dev), kc.to(dev), vc.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+        self.route = route.to(dev)
+        self.max_len = max(lens)
+        self.ws = torch.empty(ea.decode_workspace_size(len(lens), self.max_len, w.n_heads_q,
+                                                       w.head_dim), dtype=torch.uint8, device=dev)
+        self.elt = q.element_size()
+        self.bytes = metrics.decode_bytes(lens, route.tolist(), w.n_heads_kv, w.head_dim,
+                                          w.sink, w.window, self.elt)
+
+    def step(self):
+        """One decode step: lengths only on the device, as in a serving loop."""
+        w = self.w
+        ea.hybrid_attn_decode(self.q, self.kc, self.vc, self.o, self.sl, self.max_len,
+                              self.route, w.sink, w.window, self.ws)
+
+
+def decode_cpu_baseline(st: DecodeStep, seconds: float):
+    """fp64 oracle decode of whole sequences of the same batch, one at a time and cycling
+    through the batch until `seconds` of work, all cores."""
+    import oracle
+    w = st.w
+    q, kc, vc, route = st.cpu
+    threads = oracle.max_threads()
+    done, nbytes, t_used = 0, 0, 0.0
+    while t_used < seconds:
+        b = done % len(st.lens)
+        t0 = time.perf_counter()
+        oracle.decode(q[b:b + 1], kc[b:b + 1], vc[b:b + 1], st.lens[b:b + 1], w.n_heads_kv,
+                      route[b:b + 1].numpy(), w.sink, w.window)
+        t_used += time.perf_counter() - t0
+        nbytes += metrics.decode_bytes(st.lens[b:b + 1], route[b:b + 1].tolist(), w.n_heads_kv,
+                                       w.head_dim, w.sink, w.window, st.elt)
+        done += 1
+    return {"value": round(nbytes / t_used / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} single-sequence decodes cycling through the {len(st.lens)} "
+                      f"sequences of the same step ({t_used:.1f} s of fp64 oracle work)"}
+
+
+def decode_main(args):
+    st = DecodeStep(args.workload)
+    w = st.w
+    log(f"decode workload {w.name}: B={len(st.lens)} lens={st.lens[:4]}... "
+        f"sparse heads {int(st.route.sum().item())} of {st.route.numel()}")
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_events(st.step, args.steps)
+    torch.cuda.synchronize()
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {time.perf_counter() - t0:.3f} s)")
+    gbps = st.bytes / (ms * 1e-3) / 1e9
+    peak = metrics.MI355X_HBM_GBPS
+    r = st.route.cpu()
+    G = w.n_heads_q // w.n_heads_kv
+    groups_sparse = int(r.view(len(st.lens), w.n_heads_kv, G).all(dim=2).sum().item())
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if st.elt == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": len(st.lens), "cached_tokens": st.max_len,
+                   "n_heads_q": w.n_heads_q, "n_heads_kv": w.n_heads_kv,
+                   "head_dim": w.head_dim, "sink": w.sink, "window": w.window,
+                   "sparse_heads": int(r.sum().item()), "all_sparse_kv_groups": groups_sparse,
+                   "routing": f"bernoulli({w.p_sparse})"},
+        "pct_hbm_peak": round(100.0 * gbps / peak, 2),
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_split_bf16_kernel<128,4> + decode_combine_kernel",
+                     "achieved": round(gbps, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(gbps / peak, 4),
+                     "traffic": measured_traffic(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCE),
+                     "algorithmic_bytes": st.bytes, "launch_ms": round(ms, 5)},
+    }
+    if args.copy_calibration:
+        copy_calibration()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        rec["cpu_baseline"] = decode_cpu_baseline(st, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--workload", default=None,
+                    help="default qwen3_8b_32k (prefill) or decode_qwen3_8b_32k (decode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,6 +317,11 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     ea.lib()  # fail loudly if the HIP library is missing
+    if args.mode == "decode":
+        args.workload = args.workload or "decode_qwen3_8b_32k"
+        decode_main(args)
+        return
+    args.workload = args.workload or "qwen3_8b_32k"
 
     layer = Layer(args.workload)
     w = layer.w
@@ -247,12 +376,7 @@ def main():
                      "algorithmic_bytes": io, "launch_ms": round(ms_attn, 4)},
     }
     if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         rec["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)

@@ -71,13 +71,6 @@ __device__ __forceinline__ KeyRange key_range(int L, bool any_full, int sink, in
   return r;
 }
 
-__device__ __forceinline__ bool group_has_full(const uint8_t* route, int b, int Hq, int kvh,
-                                               int G) {
-  bool any = false;
-  for (int g = 0; g < G; ++g) any |= route[(int64_t)b * Hq + kvh * G + g] == 0;
-  return any;
-}
-
 // GM: compile-time bound on the group size G (query heads per KV head).
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
@@ -95,7 +88,21 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = a.seqlens[b];
   if (L < 1 || L > a.cap || L > a.max_seqlen) return;  // the combine kernel writes NaN
-  const bool any_full = group_has_full(a.route, b, Hq, kvh, G);
+  // Route bytes and q slices of the group's heads, all loads issued before any is used
+  // (head g >= G repeats head G - 1, so a bound check never serialises them).
+  const int sub = lane % LPR, rsub = lane / LPR;  // slice index, row within the pass
+  // One route byte per lane (lane l holds head min(l, G - 1)); a ballot gives every head's bit.
+  const uint8_t* rt = a.route + (int64_t)b * Hq + kvh * G;
+  const uint64_t sp_bits = __builtin_amdgcn_ballot_w64(rt[min(lane, G - 1)] != 0);
+  const bool any_full = ~sp_bits != 0;
+  u32x4 qraw[GM];
+  bool sparse[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    const int gg = min(g, G - 1);
+    sparse[g] = (sp_bits >> g) & 1;
+    qraw[g] = *(const u32x4*)((const T*)a.q + ((int64_t)b * Hq + kvh * G + gg) * D + sub * DPL);
+  }
   const KeyRange kr = key_range(L, any_full, a.sink, a.window);
   const int v0 = split * KS;
   if (v0 >= kr.n_vis) return;
@@ -109,58 +116,67 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const auto krs = make_rsrc((const T*)a.kc + base, span);
   const auto vrs = make_rsrc((const T*)a.vc + base, span);
 
-  // q slice of every head of the group, scaled by scale * log2(e)
-  const int sub = lane % LPR, rsub = lane / LPR;  // slice index, row within the pass
+  // q slices scaled by scale * log2(e), so that scores come out in log2 units
   const float c_log2 = a.scale * 1.4426950408889634f;
   float qv[GM][DPL];
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
-    if (g < G) {
-      const T* qp = (const T*)a.q + ((int64_t)b * Hq + kvh * G + g) * D + sub * DPL;
-      float f[DPL];
-      widen16<T>(*(const u32x4*)qp, f);
+    float f[DPL];
+    widen16<T>(qraw[g], f);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) qv[g][e] = f[e] * c_log2;
-    }
+    for (int e = 0; e < DPL; ++e) qv[g][e] = f[e] * c_log2;
   }
-  bool sparse[GM];
-#pragma unroll
-  for (int g = 0; g < GM; ++g)
-    sparse[g] = g < G && a.route[(int64_t)b * Hq + kvh * G + g] != 0;
 
-  // ---- scores of the split's keys: wavefront w takes local rows w*RPP + 4*RPP*p, ...
-  for (int r0 = wave * RPP; r0 < KS; r0 += 4 * RPP) {
-    const int vi = r0 + rsub;  // local index of this lane's row
-    const bool live = vi < nv;
-    const int j = live ? kr.key(v0 + vi) : 0;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (live) w = buf_load16(krs, (uint32_t)j * row_bytes + sub * 16);
-    float kf[DPL];
-    widen16<T>(w, kf);
-    float dot[GM];
+  // Each lane serves rows vi = wave*RPP + 4*RPP*p + rsub, p < NP, in chunks of CH rows whose
+  // loads are all issued before any is used (HBM latency is hidden by loads in flight, not
+  // by occupancy).  A row past the split's last visible key reads at offset `span`, outside
+  // the buffer, and gets zeros.
+  constexpr int NP = KS / (4 * RPP);
+  constexpr int CH = NP < 16 ? NP : 16;
+  auto row_off = [&](int p) __attribute__((always_inline)) {
+    const int vi = wave * RPP + 4 * RPP * p + rsub;
+    return vi < nv ? (uint32_t)kr.key(v0 + vi) * row_bytes + sub * 16 : span;
+  };
+
+  // ---- scores of the split's keys
+  u32x4 w[CH];
+  for (int p0 = 0; p0 < NP; p0 += CH) {
 #pragma unroll
-    for (int g = 0; g < GM; ++g) {
-      float acc = 0.f;
+    for (int c = 0; c < CH; ++c) w[c] = buf_load16(krs, row_off(p0 + c));
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc = __builtin_fmaf(qv[g][e], kf[e], acc);
-      dot[g] = acc;
-    }
-    // sum over the LPR lanes of the row
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1)
-#pragma unroll
-      for (int g = 0; g < GM; ++g) dot[g] += __shfl_xor(dot[g], off);
-    if (sub == 0) {
+    for (int c = 0; c < CH; ++c) {
+      const int vi = wave * RPP + 4 * RPP * (p0 + c) + rsub;
+      float kf[DPL];
+      widen16<T>(w[c], kf);
+      float dot[GM];
 #pragma unroll
       for (int g = 0; g < GM; ++g) {
-        if (g < G) {
-          // key j is visible to a sparse head iff j < sink or j > i - window
-          const bool vis = live && (!sparse[g] || j < a.sink || j > i - a.window);
-          s_p[g][vi] = vis ? dot[g] : -INFINITY;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc = __builtin_fmaf(qv[g][e], kf[e], acc);
+        dot[g] = acc;
+      }
+      // sum over the LPR lanes of the row
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1)
+#pragma unroll
+        for (int g = 0; g < GM; ++g) dot[g] += __shfl_xor(dot[g], off);
+      if (sub == 0) {
+        const int j = vi < nv ? kr.key(v0 + vi) : 0;
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+          if (g < G) {
+            // key j is visible to a sparse head iff j < sink or j > i - window
+            const bool vis = vi < nv && (!sparse[g] || j < a.sink || j > i - a.window);
+            s_p[g][vi] = vis ? dot[g] : -INFINITY;
+          }
         }
       }
     }
   }
+  // V rows of the first chunk are in flight while the softmax runs
+#pragma unroll
+  for (int c = 0; c < CH; ++c) w[c] = buf_load16(vrs, row_off(c));
   __syncthreads();
 
   // ---- per-head max, P = exp2(s - m), row sum: wavefront w takes heads w, w+4, ...
@@ -185,18 +201,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- P V: wavefront w takes the same rows as in the score pass
+  // ---- P V over the same rows (rows past the split read zeros and have P = 0)
   float acc[GM][DPL];
 #pragma unroll
   for (int g = 0; g < GM; ++g)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[g][e] = 0.f;
-  for (int r0 = wave * RPP; r0 < KS; r0 += 4 * RPP) {
-    const int vi = r0 + rsub;
-    if (vi < nv) {
-      const int j = kr.key(v0 + vi);
+  for (int p0 = 0; p0 < NP; p0 += CH) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) w[c] = buf_load16(vrs, row_off(p0 + c));
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int vi = wave * RPP + 4 * RPP * (p0 + c) + rsub;
       float vf[DPL];
-      widen16<T>(buf_load16(vrs, (uint32_t)j * row_bytes + sub * 16), vf);
+      widen16<T>(w[c], vf);
 #pragma unroll
       for (int g = 0; g < GM; ++g) {
         const float p = g < G ? s_p[g][vi] : 0.f;
@@ -233,44 +253,250 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// bf16 caches: the same split, with the scores on the matrix cores.  Wavefront w takes the
+// split's keys [64 w, 64 w + 64) as 4 blocks of 16.  Scores of a block are one
+// v_mfma_f32_16x16x32_bf16 per 32 dimensions: A = 16 keys x 32 dims, B = 32 dims x 16 query
+// heads (heads past G repeat head G - 1 and are ignored).  The dot product does not depend on
+// which dimensions fill which k slot, so lane l's A fragment is simply the 16-byte load of key
+// row (l % 16), dimension chunk 4 t + l / 16, and the q fragment uses the same chunk: every
+// operand comes straight from a load.  P V stays on the vector ALU over row-contiguous V loads
+// (lane l: row l / (D / 8), 8 dims), with the split's P read from LDS as one vector per row.
+template <int D, int GM>
+__global__ __launch_bounds__(kThreads) void decode_split_bf16_kernel(DecodeArgs a) {
+  constexpr int KS = kDecodeSplit;
+  constexpr int KW = KS / 4;          // keys per wavefront
+  constexpr int NB = KW / 16;         // 16-key blocks per wavefront
+  constexpr int NT = D / 32;          // MFMA k steps (32 dims each)
+  constexpr int LPR = D / 8;          // lanes per V row (16 bytes = 8 dims each)
+  constexpr int RPP = 64 / LPR;       // V rows per wavefront load
+  constexpr int NV = KW / RPP;        // V loads per lane
+  static_assert(GM == 1 || GM == 2 || GM == 4 || GM == 8, "group bound");
+  typedef float pvec __attribute__((ext_vector_type(GM)));
+  __shared__ pvec s_p[KS];            // P of every key, one vector of GM heads per key
+  __shared__ float s_mw[4][GM], s_lw[4][GM];
+  __shared__ float s_o[4][GM][D];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the length, the route bytes and the q fragments do not depend on one another: all three
+  // loads are in flight together
+  const int L = a.seqlens[b];
+  const uint8_t route_byte = a.route[(int64_t)b * Hq + kvh * G + min(lane, G - 1)];
+  const int n = lane & 15, kq = lane >> 4;
+  const __bf16* qh = (const __bf16*)a.q + ((int64_t)b * Hq + kvh * G + min(n, G - 1)) * D;
+  u32x4 qf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) qf[t] = *(const u32x4*)(qh + (4 * t + kq) * 8);
+  // (a length outside the contract exits here too, with no cache read; the combine kernel
+  // writes NaN for it)
+  const bool bad_len = L < 1 || L > a.cap || L > a.max_seqlen;
+  const uint64_t sp_bits = __builtin_amdgcn_ballot_w64(route_byte != 0);
+  const bool any_full = ~sp_bits != 0;
+  const KeyRange kr = key_range(L, any_full, a.sink, a.window);
+  const int v0 = split * KS;
+  if (bad_len || v0 >= kr.n_vis) return;
+  const int nv = min(KS, kr.n_vis - v0);
+  const int iq = L - 1;
+
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+  const int64_t base = ((int64_t)b * a.cap * Hkv + kvh) * D;
+  const uint32_t span = (uint32_t)(a.cap - 1) * row_bytes + D * 2;
+  const auto krs = make_rsrc((const __bf16*)a.kc + base, span);
+  const auto vrs = make_rsrc((const __bf16*)a.vc + base, span);
+  // byte offset of local key vi's row; past the split's last key: `span`, outside the buffer
+  // (loads there return zeros; span + 256 < 2^32 since span < 2^31)
+  auto row_off = [&](int vi) __attribute__((always_inline)) {
+    return vi < nv ? (uint32_t)kr.key(v0 + vi) * row_bytes : span;
+  };
+
+  // every K and V load of the split is issued here, K blocks first
+  u32x4 kf[NB][NT];
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const uint32_t off = row_off(wave * KW + 16 * blk + n);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kf[blk][t] = buf_load16(krs, off + (4 * t + kq) * 16);
+  }
+  const int vr = lane / LPR, vc = lane % LPR;
+  u32x4 vf[NV];
+#pragma unroll
+  for (int p = 0; p < NV; ++p) vf[p] = buf_load16(vrs, row_off(wave * KW + p * RPP + vr) + vc * 16);
+
+  // scores: lane l holds keys wave*KW + 16 blk + 4 (l / 16) + i of head l % 16
+  const float c_log2 = a.scale * 1.4426950408889634f;
+  const bool sp = (sp_bits >> min(n, G - 1)) & 1;
+  float sc[NB][4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[blk][t]),
+                                                    __builtin_bit_cast(bf16x8, qf[t]), acc, 0,
+                                                    0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vi = wave * KW + 16 * blk + 4 * kq + i;
+      const int j = vi < nv ? kr.key(v0 + vi) : 0;
+      // key j is visible to a sparse head iff j < sink or j > i - window
+      const bool vis = vi < nv && (!sp || j < a.sink || j > iq - a.window);
+      sc[blk][i] = vis ? acc[i] * c_log2 : -INFINITY;
+      mloc = fmaxf(mloc, sc[blk][i]);
+    }
+  }
+  // per-head max over the split: lanes n, n+16, n+32, n+48, then the 4 wavefronts
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  if (lane < GM) s_mw[wave][lane] = mloc;
+  __syncthreads();
+  const int gn = min(n, GM - 1);
+  const float M = fmaxf(fmaxf(s_mw[0][gn], s_mw[1][gn]), fmaxf(s_mw[2][gn], s_mw[3][gn]));
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float lloc = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(sc[blk][i] - Mu);
+      lloc += p;
+      if (n < GM) s_p[wave * KW + 16 * blk + 4 * kq + i][n] = p;
+    }
+  lloc += __shfl_xor(lloc, 16);
+  lloc += __shfl_xor(lloc, 32);
+  if (lane < GM) s_lw[wave][lane] = lloc;
+  __syncthreads();
+
+  // P V on the vector ALU (rows past the split read zeros and have P = 0)
+  float acc[GM][8];
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < NV; ++p) {
+    const pvec pw = s_p[wave * KW + p * RPP + vr];
+    float v[8];
+    widen16<__bf16>(vf[p], v);
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = __builtin_fmaf(pw[g], v[e], acc[g][e]);
+  }
+  // sum over the RPP rows of a load (lanes with the same chunk), then over wavefronts
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+  if (vr == 0) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][g][vc * 8 + e] = acc[g][e];
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += kThreads) {
+    const int g = x / D, d = x % D;
+    const float o = (s_o[0][g][d] + s_o[1][g][d]) + (s_o[2][g][d] + s_o[3][g][d]);
+    const int64_t bh = (int64_t)b * Hq + kvh * G + g;
+    a.o_part[(bh * a.max_splits + split) * D + d] = o;
+  }
+  if (tid < G) {
+    const int64_t bh = (int64_t)b * Hq + kvh * G + tid;
+    const float Mg = fmaxf(fmaxf(s_mw[0][tid], s_mw[1][tid]), fmaxf(s_mw[2][tid], s_mw[3][tid]));
+    a.ml_part[(bh * a.max_splits + split) * 2 + 0] = Mg;
+    a.ml_part[(bh * a.max_splits + split) * 2 + 1] =
+        (s_lw[0][tid] + s_lw[1][tid]) + (s_lw[2][tid] + s_lw[3][tid]);
+  }
+}
+
 // Per (sequence, head): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s.
-template <typename T>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int Hq = a.n_heads_q, G = Hq / a.n_heads_kv, D = a.head_dim;
+// 256 threads: a pass covers SR = 256 / (D / 4) split rows, one float4 of O_s per thread, and
+// the SR row partials are summed in LDS at the end.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int C4 = D / 4;             // float4 columns of a row
+  constexpr int SR = kThreads / C4;     // split rows per pass
+  __shared__ float s_red[kThreads / 64];
+  __shared__ f32x4 s_acc[SR][C4];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int Hq = a.n_heads_q, G = Hq / a.n_heads_kv;
   const int L = a.seqlens[b];
   const int64_t bh = (int64_t)b * Hq + h;
   T* o = (T*)a.o + bh * D;
   if (L < 1 || L > a.cap || L > a.max_seqlen) {  // outside the contract: NaN, no reads
-    for (int d = threadIdx.x; d < D; d += blockDim.x) o[d] = (T)NAN;
-    if (a.lse && threadIdx.x == 0) a.lse[bh] = NAN;
+    for (int d = tid; d < D; d += kThreads) o[d] = (T)NAN;
+    if (a.lse && tid == 0) a.lse[bh] = NAN;
     return;
   }
-  const bool any_full = group_has_full(a.route, b, Hq, h / G, G);
+  const uint8_t* rt = a.route + (int64_t)b * Hq + (h / G) * G;
+  const bool any_full = __builtin_amdgcn_ballot_w64(rt[min(tid & 63, G - 1)] == 0) != 0;
   const KeyRange kr = key_range(L, any_full, a.sink, a.window);
   const int ns = (kr.n_vis + kDecodeSplit - 1) / kDecodeSplit;
   const float* ml = a.ml_part + bh * a.max_splits * 2;
+  const f32x4* op = (const f32x4*)(a.o_part + bh * a.max_splits * D);
+
+  // M = max over splits
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s = tid; s < ns; s += kThreads) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  // split weights 2^(m_s - M) (0 for a split with no visible key) and their l-weighted sum
   float lt = 0.f;
-  for (int s = 0; s < ns; ++s)
-    if (ml[2 * s] != -INFINITY) lt += ml[2 * s + 1] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
-  const float inv = 1.0f / lt;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s)
-      if (ml[2 * s] != -INFINITY)
-        acc += a.o_part[(bh * a.max_splits + s) * D + d] * __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    o[d] = (T)(acc * inv);
+  for (int s = tid; s < ns; s += kThreads) {
+    const float m = ml[2 * s];
+    if (m != -INFINITY) lt += ml[2 * s + 1] * __builtin_amdgcn_exp2f(m - M);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
+  if ((tid & 63) == 0) s_red[tid >> 6] = lt;
+  __syncthreads();
+  lt = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+
+  // weighted sum of the splits' O rows
+  const int c = tid % C4, r = tid / C4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = r; s < ns; s += SR) {
+    const float m = ml[2 * s];
+    const float wgt = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    const f32x4 x = op[(int64_t)s * C4 + c];
+    acc += wgt * x;
+  }
+  s_acc[r][c] = acc;
+  __syncthreads();
+  if (tid < C4) {
+    f32x4 t = s_acc[0][tid];
+#pragma unroll
+    for (int rr = 1; rr < SR; ++rr) t += s_acc[rr][tid];
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[4 * tid + e] = (T)(t[e] * inv);
   }
   // scores were in log2 units: lse = (M + log2 l) * ln 2
-  if (a.lse && threadIdx.x == 0) a.lse[bh] = (M + log2f(lt)) * 0.6931471805599453f;
+  if (a.lse && tid == 0) a.lse[bh] = (M + log2f(lt)) * 0.6931471805599453f;
 }
 
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, int G, hipStream_t stream) {
   const dim3 grid(a.max_splits, a.n_heads_kv, a.batch);
-  if (G <= 1)
+  if constexpr (sizeof(T) == 2) {
+    if (G <= 1)
+      decode_split_bf16_kernel<D, 1><<<grid, kThreads, 0, stream>>>(a);
+    else if (G <= 2)
+      decode_split_bf16_kernel<D, 2><<<grid, kThreads, 0, stream>>>(a);
+    else if (G <= 4)
+      decode_split_bf16_kernel<D, 4><<<grid, kThreads, 0, stream>>>(a);
+    else
+      decode_split_bf16_kernel<D, 8><<<grid, kThreads, 0, stream>>>(a);
+  } else if (G <= 1)
     decode_split_kernel<T, D, 1><<<grid, kThreads, 0, stream>>>(a);
   else if (G <= 2)
     decode_split_kernel<T, D, 2><<<grid, kThreads, 0, stream>>>(a);
@@ -280,7 +506,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, int G, hipStream_t stream) {
     decode_split_kernel<T, D, 8><<<grid, kThreads, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<T><<<dim3(a.n_heads_q, a.batch), 128, 0, stream>>>(a);
+  decode_combine_kernel<T, D><<<dim3(a.n_heads_q, a.batch), kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -48,5 +48,33 @@ def io_bytes(total_tokens: int, n_heads_q: int, n_heads_kv: int, head_dim: int,
     return int(total_tokens) * int(head_dim) * int(elem_bytes) * (2 * n_heads_q + 2 * n_heads_kv)
 
 
+def decode_group_keys(length: int, all_sparse: bool, sink: int, window: int) -> int:
+    """Cache rows a KV-head group must read for the query at i = L - 1: all L when any
+    query head of the group is full; otherwise the window min(W, L) plus the sink keys
+    below it, min(s, L - W) when L > W."""
+    L, s, W = int(length), int(sink), int(window)
+    if L <= 0:
+        return 0
+    if not all_sparse:
+        return L
+    return min(W, L) + min(s, max(0, L - W))
+
+
+def decode_bytes(lengths, route, n_heads_kv: int, head_dim: int, sink: int, window: int,
+                 elem_bytes: int) -> int:
+    """Algorithmic HBM bytes of one decode step: for every sequence and KV head, the K and
+    V rows its group of query heads sees, read once; plus q read and o written."""
+    total = 0
+    for b, L in enumerate(lengths):
+        r = [int(x) for x in route[b]]
+        G = len(r) // int(n_heads_kv)
+        for kvh in range(int(n_heads_kv)):
+            grp = r[kvh * G:(kvh + 1) * G]
+            n = decode_group_keys(L, all(grp), sink, window)
+            total += 2 * n * int(head_dim) * int(elem_bytes)
+        total += 2 * len(r) * int(head_dim) * int(elem_bytes)
+    return total
+
+
 MI355X_BF16_DENSE_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense (no sparsity)
 MI355X_HBM_GBPS = 8000.0

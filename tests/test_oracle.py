@@ -355,6 +355,20 @@ def test_visible_pair_closed_form(L, sink, window):
             lib_mask(L, sparse, sink, window).sum())
 
 
+@pytest.mark.parametrize("L,sink,window", [(1, 0, 1), (10, 3, 4), (50, 0, 7), (64, 64, 1),
+                                           (33, 5, 40), (200, 17, 31), (300, 300, 5)])
+def test_decode_group_keys_is_union_of_last_rows(L, sink, window):
+    """Rows a group reads = keys visible to the last query row under any head of the group."""
+    full_last = lib_mask(L, False, sink, window)[L - 1]
+    sparse_last = lib_mask(L, True, sink, window)[L - 1]
+    assert metrics.decode_group_keys(L, True, sink, window) == int(sparse_last.sum())
+    assert metrics.decode_group_keys(L, False, sink, window) == int((full_last | sparse_last).sum())
+    lens, route = [L, 3], [[1, 1, 0, 1], [1, 1, 1, 1]]
+    want = 2 * 8 * 2 * (int(sparse_last.sum()) + L
+                        + metrics.decode_group_keys(3, True, sink, window) * 2) + 2 * 2 * 4 * 8 * 2
+    assert metrics.decode_bytes(lens, route, 2, 8, sink, window, 2) == want
+
+
 # ---- decode step (one new query per sequence over its KV cache) ----
 
 def make_cache(lens, cap, hq, hkv, d, seed, poison=True):
