@@ -425,7 +425,7 @@ ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* 
   if (ws_bytes < need) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_decode_workspace_size()");
   const int64_t splits = ceil_div64(max_seqlen, kDecodeSplit);
   if (splits > 2147483647 / 2) return fail(EA_ERR_UNSUPPORTED, "too many splits");
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;
   a.vc = v_cache;
@@ -448,6 +448,193 @@ ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* 
   a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
   const hipError_t e = launch_decode(a, dt == EA_BF16, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return EA_OK;
+}
+
+ea_status ea_decode_pool_layout(const uint8_t* route_host, int32_t batch, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t capacity, int32_t sink,
+                                int32_t window, int64_t* region_base_host,
+                                int32_t* region_rows_host, int64_t* total_rows_host) {
+  g_last_error.clear();
+  int64_t* const region_base = region_base_host;
+  int32_t* const region_rows = region_rows_host;
+  int64_t* const total_rows = total_rows_host;
+  if (!route_host || !region_base || !region_rows || !total_rows)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (batch < 1 || capacity < 1) return fail(EA_ERR_INVALID_ARG, "need batch >= 1 and capacity >= 1");
+  if (n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(EA_ERR_INVALID_ARG, "n_heads_q must be a positive multiple of n_heads_kv");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  if ((int64_t)sink + window > 2147483647) return fail(EA_ERR_INVALID_ARG, "sink + window overflows");
+  const int G = n_heads_q / n_heads_kv;
+  int64_t next = 0;
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t h = 0; h < n_heads_kv; ++h) {
+      bool any_full = false;
+      for (int g = 0; g < G; ++g) any_full |= route_host[(int64_t)b * n_heads_q + h * G + g] == 0;
+      const int32_t rows = any_full ? capacity : sink + window;
+      region_base[(int64_t)b * n_heads_kv + h] = next;
+      region_rows[(int64_t)b * n_heads_kv + h] = rows;
+      next += rows;
+    }
+  *total_rows = next;
+  return EA_OK;
+}
+
+// checks shared by the pooled-cache entry points
+static ea_status check_pool_args(ea_dtype dt, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
+                                 int32_t head_dim, int32_t sink, int32_t window, int64_t pool_rows,
+                                 const void* k_pool, const void* v_pool) {
+  if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1) return fail(EA_ERR_INVALID_ARG, "need batch >= 1");
+  if (n_heads_q < 1 || n_heads_kv < 1 || n_heads_q % n_heads_kv != 0)
+    return fail(EA_ERR_INVALID_ARG, "n_heads_q must be a positive multiple of n_heads_kv");
+  if (n_heads_q / n_heads_kv > kDecodeMaxGroup)
+    return fail(EA_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (head_dim != 64 && head_dim != 128) return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  if ((int64_t)sink + window > 2147483647) return fail(EA_ERR_INVALID_ARG, "sink + window overflows");
+  if (pool_rows < 1) return fail(EA_ERR_INVALID_ARG, "need pool_rows >= 1");
+  if (!aligned16(k_pool) || !aligned16(v_pool))
+    return fail(EA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  const int64_t row_bytes = (int64_t)head_dim * (dt == EA_BF16 ? 2 : 4);
+  if (overlaps(k_pool, (size_t)(pool_rows * row_bytes), v_pool, (size_t)(pool_rows * row_bytes)))
+    return fail(EA_ERR_INVALID_ARG, "k_pool and v_pool overlap");
+  return EA_OK;
+}
+
+ea_status ea_decode_pool_fill(const void* k, const void* v, ea_dtype dt, const int32_t* cu_seqlens,
+                              int32_t batch, int32_t max_seqlen, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                              int32_t sink, int32_t window, const int64_t* region_base,
+                              const int32_t* region_rows, int64_t pool_rows, void* k_pool,
+                              void* v_pool, void* stream) {
+  g_last_error.clear();
+  if (!k || !v || !cu_seqlens || !route || !region_base || !region_rows || !k_pool || !v_pool)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  const ea_status st = check_pool_args(dt, batch, n_heads_q, n_heads_kv, head_dim, sink, window,
+                                       pool_rows, k_pool, v_pool);
+  if (st != EA_OK) return st;
+  if (max_seqlen < 1) return fail(EA_ERR_INVALID_ARG, "need max_seqlen >= 1");
+  if (!aligned16(k) || !aligned16(v)) return fail(EA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  PoolWriteArgs a{};
+  a.k = k;
+  a.v = v;
+  a.cu = cu_seqlens;
+  a.route = route;
+  a.region_base = region_base;
+  a.region_rows = region_rows;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.pool_rows = pool_rows;
+  a.batch = batch;
+  a.max_seqlen = max_seqlen;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  const hipError_t e = launch_pool_fill(a, dt == EA_BF16 ? 2 : 4, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pool fill launch");
+  return EA_OK;
+}
+
+ea_status ea_decode_pool_append(const void* k_new, const void* v_new, ea_dtype dt,
+                                const int32_t* positions, int32_t batch, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                                int32_t sink, int32_t window, const int64_t* region_base,
+                                const int32_t* region_rows, int64_t pool_rows, void* k_pool,
+                                void* v_pool, void* stream) {
+  g_last_error.clear();
+  if (!k_new || !v_new || !positions || !route || !region_base || !region_rows || !k_pool || !v_pool)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  const ea_status st = check_pool_args(dt, batch, n_heads_q, n_heads_kv, head_dim, sink, window,
+                                       pool_rows, k_pool, v_pool);
+  if (st != EA_OK) return st;
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(EA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  PoolWriteArgs a{};
+  a.k = k_new;
+  a.v = v_new;
+  a.positions = positions;
+  a.route = route;
+  a.region_base = region_base;
+  a.region_rows = region_rows;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.pool_rows = pool_rows;
+  a.batch = batch;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  const hipError_t e = launch_pool_append(a, dt == EA_BF16 ? 2 : 4, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pool append launch");
+  return EA_OK;
+}
+
+ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const void* v_pool,
+                                     void* o, ea_dtype dt, const int32_t* seqlens,
+                                     const int32_t* seqlens_host, int32_t batch,
+                                     int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                     int32_t head_dim, const int64_t* region_base,
+                                     const int32_t* region_rows, int64_t pool_rows,
+                                     const uint8_t* route, int32_t sink, int32_t window,
+                                     float scale, float* lse_out, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k_pool || !v_pool || !o || !seqlens || !route || !workspace || !region_base ||
+      !region_rows)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  const ea_status st = check_pool_args(dt, batch, n_heads_q, n_heads_kv, head_dim, sink, window,
+                                       pool_rows, k_pool, v_pool);
+  if (st != EA_OK) return st;
+  if (max_seqlen < 1) return fail(EA_ERR_INVALID_ARG, "need max_seqlen >= 1");
+  if (isnan(scale) || isinf(scale)) return fail(EA_ERR_INVALID_ARG, "scale is not finite");
+  if (!aligned16(q) || !aligned16(o)) return fail(EA_ERR_INVALID_ARG, "q and o must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0) return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const int64_t elem = dt == EA_BF16 ? 2 : 4;
+  const size_t qo_bytes = (size_t)batch * n_heads_q * head_dim * elem;
+  const size_t pool_bytes = (size_t)pool_rows * head_dim * elem;
+  if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(o, qo_bytes, k_pool, pool_bytes) ||
+      overlaps(o, qo_bytes, v_pool, pool_bytes))
+    return fail(EA_ERR_INVALID_ARG, "o overlaps q or a pool");
+  if (seqlens_host)
+    for (int32_t b = 0; b < batch; ++b)
+      if (seqlens_host[b] < 1 || seqlens_host[b] > max_seqlen)
+        return fail(EA_ERR_INVALID_ARG, "seqlens must lie in [1, max_seqlen]");
+  const size_t need = ea_decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim);
+  if (need == 0) return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < need) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_decode_workspace_size()");
+  const int64_t splits = ceil_div64(max_seqlen, kDecodeSplit);
+  DecodeArgs a{};
+  a.q = q;
+  a.kc = k_pool;
+  a.vc = v_pool;
+  a.o = o;
+  a.seqlens = seqlens;
+  a.route = route;
+  a.region_base = region_base;
+  a.region_rows = region_rows;
+  a.pool_rows = pool_rows;
+  a.pooled = 1;
+  a.o_part = (float*)workspace;
+  a.ml_part = (float*)((char*)workspace +
+                       align256((size_t)batch * n_heads_q * splits * head_dim * 4));
+  a.lse = lse_out;
+  a.batch = batch;
+  a.cap = max_seqlen;  // lengths are bounded by max_seqlen; each region's size by its own check
+  a.max_seqlen = max_seqlen;
+  a.max_splits = (int)splits;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+  const hipError_t e = launch_decode(a, dt == EA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pooled decode launch");
   return EA_OK;
 }
 

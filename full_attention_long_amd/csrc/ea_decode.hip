@@ -71,6 +71,61 @@ __device__ __forceinline__ KeyRange key_range(int L, bool any_full, int sink, in
   return r;
 }
 
+// Where the cached rows of one (sequence, KV head) live, and which row holds key j.
+//   dense cache [batch, cap, Hkv, D]: key j at row j of the sequence, rows Hkv * D apart;
+//   pooled cache [pool_rows, D]: the (b, kvh) region, rows D apart; a KV head with a full
+//   query head keeps key j at row j, an all-sparse one the sink keys at rows j < sink and
+//   the window in a ring of `window` rows: key j >= sink at row sink + (j - sink) % window.
+//   The window keys of the query are consecutive, so the ring rows of those >= jb follow
+//   from one remainder ra = (jb - sink) % window with a single wrap.
+struct CacheView {
+  int64_t elem0;        // element offset of row 0 in the K and V arrays
+  uint32_t row_bytes;   // bytes between consecutive rows
+  uint32_t span;        // bytes of the region (reads past it return zeros)
+  int sink, window, jb, ra;
+  bool ring, ok;
+  __device__ __forceinline__ uint32_t row(int j) const {
+    if (!ring || j < sink) return (uint32_t)j;
+    const int t = ra + (j - jb);
+    return (uint32_t)(sink + (t >= window ? t - window : t));
+  }
+};
+
+// Pooled region of (b, kvh) and whether it can serve a query at L - 1: its rows lie in the
+// pool, stay within 32-bit byte offsets, and hold every key the query can see (all L for a
+// group with a full head, sink + window rows for a ring).
+template <int D, int ELT>
+__device__ __forceinline__ CacheView cache_view(const DecodeArgs& a, int b, int kvh, int L,
+                                                bool any_full, const KeyRange& kr) {
+  CacheView c;
+  c.sink = a.sink;
+  c.window = a.window;
+  c.ring = false;
+  c.jb = 0;
+  c.ra = 0;
+  if (!a.pooled) {
+    c.elem0 = ((int64_t)b * a.cap * a.n_heads_kv + kvh) * D;
+    c.row_bytes = (uint32_t)a.n_heads_kv * D * ELT;
+    c.span = (uint32_t)(a.cap - 1) * c.row_bytes + D * ELT;
+    c.ok = true;
+    return c;
+  }
+  const int64_t base = a.region_base[(int64_t)b * a.n_heads_kv + kvh];
+  const int32_t rows = a.region_rows[(int64_t)b * a.n_heads_kv + kvh];
+  const int64_t need = any_full ? (int64_t)L : (int64_t)a.sink + a.window;
+  c.ok = base >= 0 && rows >= 1 && base + rows <= a.pool_rows &&
+         (int64_t)rows * D * ELT < ((int64_t)1 << 31) && rows >= need;
+  c.elem0 = c.ok ? base * D : 0;
+  c.row_bytes = D * ELT;
+  c.span = c.ok ? (uint32_t)rows * D * ELT : 0;
+  if (!any_full) {
+    c.ring = true;
+    c.jb = max(kr.win_start, a.sink);
+    c.ra = (c.jb - a.sink) % a.window;
+  }
+  return c;
+}
+
 // GM: compile-time bound on the group size G (query heads per KV head).
 template <typename T, int D, int GM>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
@@ -104,17 +159,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     qraw[g] = *(const u32x4*)((const T*)a.q + ((int64_t)b * Hq + kvh * G + gg) * D + sub * DPL);
   }
   const KeyRange kr = key_range(L, any_full, a.sink, a.window);
+  const CacheView cv = cache_view<D, ELT>(a, b, kvh, L, any_full, kr);
   const int v0 = split * KS;
-  if (v0 >= kr.n_vis) return;
+  if (!cv.ok || v0 >= kr.n_vis) return;  // a region that cannot serve the query: NaN outputs
   const int nv = min(KS, kr.n_vis - v0);
   const int i = L - 1;
 
-  // this sequence's rows of KV head kvh: row j at byte j * Hkv * D * ELT
-  const uint32_t row_bytes = (uint32_t)Hkv * D * ELT;
-  const int64_t base = ((int64_t)b * a.cap * Hkv + kvh) * D;
-  const uint32_t span = (uint32_t)(a.cap - 1) * row_bytes + D * ELT;
-  const auto krs = make_rsrc((const T*)a.kc + base, span);
-  const auto vrs = make_rsrc((const T*)a.vc + base, span);
+  const uint32_t row_bytes = cv.row_bytes, span = cv.span;
+  const auto krs = make_rsrc((const T*)a.kc + cv.elem0, span);
+  const auto vrs = make_rsrc((const T*)a.vc + cv.elem0, span);
 
   // q slices scaled by scale * log2(e), so that scores come out in log2 units
   const float c_log2 = a.scale * 1.4426950408889634f;
@@ -135,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int CH = NP < 16 ? NP : 16;
   auto row_off = [&](int p) __attribute__((always_inline)) {
     const int vi = wave * RPP + 4 * RPP * p + rsub;
-    return vi < nv ? (uint32_t)kr.key(v0 + vi) * row_bytes + sub * 16 : span;
+    return vi < nv ? cv.row(kr.key(v0 + vi)) * row_bytes + sub * 16 : span;
   };
 
   // ---- scores of the split's keys
@@ -294,20 +347,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_bf16_kernel(DecodeArgs 
   const uint64_t sp_bits = __builtin_amdgcn_ballot_w64(route_byte != 0);
   const bool any_full = ~sp_bits != 0;
   const KeyRange kr = key_range(L, any_full, a.sink, a.window);
+  const CacheView cv = cache_view<D, 2>(a, b, kvh, L, any_full, kr);
   const int v0 = split * KS;
-  if (bad_len || v0 >= kr.n_vis) return;
+  if (bad_len || !cv.ok || v0 >= kr.n_vis) return;
   const int nv = min(KS, kr.n_vis - v0);
   const int iq = L - 1;
 
-  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
-  const int64_t base = ((int64_t)b * a.cap * Hkv + kvh) * D;
-  const uint32_t span = (uint32_t)(a.cap - 1) * row_bytes + D * 2;
-  const auto krs = make_rsrc((const __bf16*)a.kc + base, span);
-  const auto vrs = make_rsrc((const __bf16*)a.vc + base, span);
+  const uint32_t row_bytes = cv.row_bytes, span = cv.span;
+  const auto krs = make_rsrc((const __bf16*)a.kc + cv.elem0, span);
+  const auto vrs = make_rsrc((const __bf16*)a.vc + cv.elem0, span);
   // byte offset of local key vi's row; past the split's last key: `span`, outside the buffer
   // (loads there return zeros; span + 256 < 2^32 since span < 2^31)
   auto row_off = [&](int vi) __attribute__((always_inline)) {
-    return vi < nv ? (uint32_t)kr.key(v0 + vi) * row_bytes : span;
+    return vi < nv ? cv.row(kr.key(v0 + vi)) * row_bytes : span;
   };
 
   // every K and V load of the split is issued here, K blocks first
@@ -435,6 +487,11 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   const uint8_t* rt = a.route + (int64_t)b * Hq + (h / G) * G;
   const bool any_full = __builtin_amdgcn_ballot_w64(rt[min(tid & 63, G - 1)] == 0) != 0;
   const KeyRange kr = key_range(L, any_full, a.sink, a.window);
+  if (!cache_view<D, sizeof(T)>(a, b, h / G, L, any_full, kr).ok) {  // no usable region: NaN
+    for (int d = tid; d < D; d += kThreads) o[d] = (T)NAN;
+    if (a.lse && tid == 0) a.lse[bh] = NAN;
+    return;
+  }
   const int ns = (kr.n_vis + kDecodeSplit - 1) / kDecodeSplit;
   const float* ml = a.ml_part + bh * a.max_splits * 2;
   const f32x4* op = (const f32x4*)(a.o_part + bh * a.max_splits * D);
@@ -484,6 +541,67 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a) 
   if (a.lse && tid == 0) a.lse[bh] = (M + log2f(lt)) * 0.6931471805599453f;
 }
 
+// ---- pooled cache writers
+
+// Region of (b, kvh) and the row of position j in it, or -1 where the position is not kept
+// (a ring keeps the sink and the last `window` positions before `upto`) or the region is
+// unusable (outside the pool, or too small for the row).
+__device__ __forceinline__ int64_t pool_row(const PoolWriteArgs& a, int b, int kvh, int j,
+                                            int upto, int row_bytes) {
+  const int G = a.n_heads_q / a.n_heads_kv;
+  const uint8_t* rt = a.route + (int64_t)b * a.n_heads_q + kvh * G;
+  bool any_full = false;
+  for (int g = 0; g < G; ++g) any_full |= rt[g] == 0;
+  const int64_t base = a.region_base[(int64_t)b * a.n_heads_kv + kvh];
+  const int32_t rows = a.region_rows[(int64_t)b * a.n_heads_kv + kvh];
+  if (base < 0 || rows < 1 || base + rows > a.pool_rows ||
+      (int64_t)rows * row_bytes >= ((int64_t)1 << 31) || j < 0)
+    return -1;
+  int64_t r;
+  if (any_full) {
+    r = j;
+  } else {
+    if (!(j < a.sink || j >= upto - a.window)) return -1;
+    r = j < a.sink ? j : a.sink + (j - a.sink) % a.window;
+  }
+  return r < rows ? base + r : -1;
+}
+
+// Prefill K/V of packed sequences into the pool: workgroup (block of 64 positions, kvh, b),
+// one 16-byte chunk of a K or V row per thread.
+__global__ __launch_bounds__(256) void pool_fill_kernel(PoolWriteArgs a, int row_bytes) {
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int seq0 = a.cu[b], L = a.cu[b + 1] - seq0;
+  const int chunks = row_bytes / 16, rpp = 256 / chunks;
+  const int c = threadIdx.x % chunks;
+  const int j1 = min(L, (int)(blockIdx.x + 1) * 64);
+  for (int j = blockIdx.x * 64 + threadIdx.x / chunks; j < j1; j += rpp) {
+    const int64_t r = pool_row(a, b, kvh, j, L, row_bytes);
+    if (r < 0) continue;
+    const int64_t src = ((int64_t)(seq0 + j) * a.n_heads_kv + kvh) * row_bytes + c * 16;
+    const int64_t dst = r * row_bytes + c * 16;
+    *(u32x4*)((char*)a.k_pool + dst) = *(const u32x4*)((const char*)a.k + src);
+    *(u32x4*)((char*)a.v_pool + dst) = *(const u32x4*)((const char*)a.v + src);
+  }
+}
+
+// One new K/V row per (sequence, KV head), at position positions[b] (the ring keeps it as the
+// newest of its window); workgroup (kvh, b), one 16-byte chunk per thread (K then V).
+__global__ __launch_bounds__(64) void pool_append_kernel(PoolWriteArgs a, int row_bytes) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int j = a.positions[b];
+  const int64_t r = pool_row(a, b, kvh, j, j + 1, row_bytes);
+  const int chunks = row_bytes / 16;
+  const int t = threadIdx.x;
+  if (r < 0 || t >= 2 * chunks) return;
+  const bool is_v = t >= chunks;
+  const int c = is_v ? t - chunks : t;
+  const int64_t src = ((int64_t)b * a.n_heads_kv + kvh) * row_bytes + c * 16;
+  const int64_t dst = r * row_bytes + c * 16;
+  *(u32x4*)((char*)(is_v ? a.v_pool : a.k_pool) + dst) =
+      *(const u32x4*)((const char*)(is_v ? a.v : a.k) + src);
+}
+
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, int G, hipStream_t stream) {
   const dim3 grid(a.max_splits, a.n_heads_kv, a.batch);
@@ -511,6 +629,19 @@ hipError_t launch_decode_t(const DecodeArgs& a, int G, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_pool_fill(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream) {
+  const int row_bytes = a.head_dim * elem_bytes;
+  const dim3 grid((a.max_seqlen + 63) / 64, a.n_heads_kv, a.batch);
+  pool_fill_kernel<<<grid, 256, 0, stream>>>(a, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_append(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream) {
+  const int row_bytes = a.head_dim * elem_bytes;
+  pool_append_kernel<<<dim3(a.n_heads_kv, a.batch), 64, 0, stream>>>(a, row_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream) {
   const int G = a.n_heads_q / a.n_heads_kv;

@@ -81,8 +81,16 @@ constexpr int kDecodeSplit = 256;
 constexpr int kDecodeMaxGroup = 8;
 struct DecodeArgs {
   const void* q;          // [batch, n_heads_q, head_dim]
-  const void* kc;         // [batch, cap, n_heads_kv, head_dim]
+  const void* kc;         // dense: [batch, cap, n_heads_kv, head_dim]; pooled: [pool_rows, head_dim]
   const void* vc;
+  // pooled cache (pooled != 0): the rows of (sequence b, KV head h) start at row
+  // region_base[b * n_heads_kv + h] of the pool and number region_rows[...]; a KV head with a
+  // full query head keeps position j at row j, one whose query heads are all sparse keeps
+  // the sink and a ring of `window` rows (position j >= sink at row sink + (j - sink) % window)
+  const int64_t* region_base;
+  const int32_t* region_rows;
+  int64_t pool_rows;
+  int pooled;
   void* o;                // [batch, n_heads_q, head_dim]
   const int32_t* seqlens; // [batch]
   const uint8_t* route;   // [batch, n_heads_q]
@@ -93,6 +101,24 @@ struct DecodeArgs {
   float scale;
 };
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t stream);
+// Pooled cache writers (ea_decode.hip).  fill: prefill K/V [T, n_heads_kv, head_dim] of
+// packed sequences (cu) into their regions, every row the next decode step can see;
+// append: one new row per (sequence, KV head) at position positions[b].
+struct PoolWriteArgs {
+  const void* k;          // fill: [T, n_heads_kv, head_dim]; append: [batch, n_heads_kv, head_dim]
+  const void* v;
+  const int32_t* cu;      // fill: [batch + 1]
+  const int32_t* positions;  // append: [batch]
+  const uint8_t* route;   // [batch, n_heads_q]
+  const int64_t* region_base;
+  const int32_t* region_rows;
+  void* k_pool;
+  void* v_pool;
+  int64_t pool_rows;
+  int batch, max_seqlen, n_heads_q, n_heads_kv, head_dim, sink, window;
+};
+hipError_t launch_pool_fill(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);
+hipError_t launch_pool_append(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);
 
 // Workgroups of each attention kernel that fit on one CU at once.
 int attn_bf16_blocks_per_cu();

@@ -19,7 +19,8 @@ EA_BF16, EA_F32 = 0, 1
 
 EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_error",
            "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run",
-           "ea_decode_workspace_size", "ea_hybrid_attn_decode")
+           "ea_decode_workspace_size", "ea_hybrid_attn_decode", "ea_decode_pool_layout",
+           "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool")
 
 _lib = None
 
@@ -65,6 +66,17 @@ def lib():
     L.ea_hybrid_attn_decode.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, P,
                                         i32, i32, f32, P, P, sz, P]
     L.ea_hybrid_attn_decode.restype = i32
+    L.ea_decode_pool_layout.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P]
+    L.ea_decode_pool_layout.restype = i32
+    L.ea_decode_pool_fill.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32, P, P,
+                                      i64, P, P, P]
+    L.ea_decode_pool_fill.restype = i32
+    L.ea_decode_pool_append.argtypes = [P, P, i32, P, i32, i32, i32, i32, P, i32, i32, P, P, i64,
+                                        P, P, P]
+    L.ea_decode_pool_append.restype = i32
+    L.ea_hybrid_attn_decode_pool.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P,
+                                             i64, P, i32, i32, f32, P, P, sz, P]
+    L.ea_hybrid_attn_decode_pool.restype = i32
     _lib = L
     return L
 
@@ -203,3 +215,57 @@ def hybrid_attn_decode(q, k_cache, v_cache, o, seqlens, max_seqlen, route_bits, 
                                        _ptr(lse_out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+
+
+def decode_pool_layout(route_host, n_heads_kv, capacity, sink, window):
+    """ea_decode_pool_layout on a host routing [B, Hq] (uint8 tensor or array): returns
+    (region_base int64 [B*Hkv], region_rows int32 [B*Hkv], total_rows) as CPU tensors / int."""
+    import numpy as np
+    import torch
+    r = np.ascontiguousarray(np.asarray(route_host, dtype=np.uint8))
+    batch, hq = r.shape
+    base = torch.empty(batch * n_heads_kv, dtype=torch.int64)
+    rows = torch.empty(batch * n_heads_kv, dtype=torch.int32)
+    total = ctypes.c_int64(0)
+    _check(lib().ea_decode_pool_layout(r.ctypes.data, batch, hq, n_heads_kv, capacity, sink, window,
+                                       base.data_ptr(), rows.data_ptr(), ctypes.byref(total)))
+    return base, rows, int(total.value)
+
+
+def decode_pool_fill(k, v, cu_seqlens, max_seqlen, n_heads_q, route_bits, sink, window,
+                     region_base, region_rows, k_pool, v_pool, stream=None):
+    """ea_decode_pool_fill: k/v [T, Hkv, D] packed by cu_seqlens into k_pool/v_pool [rows, D]."""
+    _check(lib().ea_decode_pool_fill(_ptr(k), _ptr(v), dtype_code(k.dtype), _ptr(cu_seqlens),
+                                     cu_seqlens.numel() - 1, max_seqlen, n_heads_q, k.shape[1],
+                                     k.shape[2], _ptr(route_bits), sink, window,
+                                     _ptr(region_base), _ptr(region_rows), k_pool.shape[0],
+                                     _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+
+def decode_pool_append(k_new, v_new, positions, n_heads_q, route_bits, sink, window,
+                       region_base, region_rows, k_pool, v_pool, stream=None):
+    """ea_decode_pool_append: k_new/v_new [B, Hkv, D] at positions [B] (int32 device)."""
+    _check(lib().ea_decode_pool_append(_ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype),
+                                       _ptr(positions), k_new.shape[0], n_heads_q, k_new.shape[1],
+                                       k_new.shape[2], _ptr(route_bits), sink, window,
+                                       _ptr(region_base), _ptr(region_rows), k_pool.shape[0],
+                                       _ptr(k_pool), _ptr(v_pool), _stream(stream)))
+
+
+def hybrid_attn_decode_pool(q, k_pool, v_pool, o, seqlens, max_seqlen, n_heads_kv, region_base,
+                            region_rows, route_bits, sink, window, workspace, scale=0.0,
+                            seqlens_host=None, lse_out=None, stream=None):
+    """ea_hybrid_attn_decode_pool: q/o [B, Hq, D]; k_pool/v_pool [rows, D]; regions from
+    decode_pool_layout (device copies)."""
+    batch = q.shape[0]
+    host = None
+    if seqlens_host is not None:
+        host = (ctypes.c_int32 * batch)(*[int(x) for x in seqlens_host])
+    _check(lib().ea_hybrid_attn_decode_pool(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(o),
+                                            dtype_code(q.dtype), _ptr(seqlens), host, batch,
+                                            max_seqlen, q.shape[1], n_heads_kv, q.shape[2],
+                                            _ptr(region_base), _ptr(region_rows), k_pool.shape[0],
+                                            _ptr(route_bits), sink, window, float(scale),
+                                            _ptr(lse_out), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))

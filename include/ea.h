@@ -213,6 +213,80 @@ ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* 
                                 int32_t sink, int32_t window, float scale, float* lse_out,
                                 void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Pooled KV cache for decode.  A KV head whose query heads are all sparse only ever needs
+ * the sink keys and the last `window` keys (the sparse pattern above), so its cache can be a
+ * sink + ring buffer of sink + window rows instead of a full history; this is where the
+ * hybrid routing saves decode memory.  The pool is one array of rows per tensor,
+ * k_pool / v_pool [pool_rows, head_dim], dtype dt; the rows of (sequence b, KV head h) form
+ * the region region_base[b * n_heads_kv + h] .. + region_rows[...] (int64 / int32, device
+ * for the kernels):
+ *   linear region (some query head of h is full, route == 0): position j at row j;
+ *   ring region (every query head of h is sparse): position j < sink at row j, position
+ *     j >= sink at row sink + (j - sink) % window; it needs sink + window rows.
+ * The routing must be the one the regions were laid out for.
+ */
+
+/*
+ * Host-only layout of a pool: for route_host [batch, n_heads_q] (uint8, host), linear
+ * regions of `capacity` rows and ring regions of sink + window rows, packed in (b, h) order
+ * from row 0.  Writes region_base_host / region_rows_host [batch * n_heads_kv] and
+ * *total_rows_host (the pool_rows to allocate).  batch >= 1, capacity >= 1, sink >= 0,
+ * window >= 1, n_heads_q a multiple of n_heads_kv.
+ */
+ea_status ea_decode_pool_layout(const uint8_t* route_host, int32_t batch, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t capacity, int32_t sink,
+                                int32_t window, int64_t* region_base_host,
+                                int32_t* region_rows_host, int64_t* total_rows_host);
+
+/*
+ * Prefill K/V into the pool: k, v [T, n_heads_kv, head_dim] packed as cu_seqlens [batch+1]
+ * (max_seqlen >= every length).  A linear region receives every position (those past its
+ * rows are dropped); a ring region receives the positions a decode query at position L can
+ * see besides its own: j < sink and j >= L - window, L the sequence length.  A region outside
+ * the pool or beyond 2^31 bytes is skipped (the decode then gives NaN for it).  head_dim 64
+ * or 128; at most 8 query heads per KV head; k, v, pools 16-byte aligned.
+ */
+ea_status ea_decode_pool_fill(const void* k, const void* v, ea_dtype dt, const int32_t* cu_seqlens,
+                              int32_t batch, int32_t max_seqlen, int32_t n_heads_q,
+                              int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                              int32_t sink, int32_t window, const int64_t* region_base,
+                              const int32_t* region_rows, int64_t pool_rows, void* k_pool,
+                              void* v_pool, void* stream);
+
+/*
+ * Append one token per sequence: k_new, v_new [batch, n_heads_kv, head_dim] go to position
+ * positions[b] (int32 device; the new length minus one) of every region of sequence b; in a
+ * ring the row of position j - window is reused, which no later query can see.  A negative
+ * position, a row past the region or an unusable region writes nothing.  Call it before
+ * ea_hybrid_attn_decode_pool for that token (the query's own key is part of its cache).
+ */
+ea_status ea_decode_pool_append(const void* k_new, const void* v_new, ea_dtype dt,
+                                const int32_t* positions, int32_t batch, int32_t n_heads_q,
+                                int32_t n_heads_kv, int32_t head_dim, const uint8_t* route,
+                                int32_t sink, int32_t window, const int64_t* region_base,
+                                const int32_t* region_rows, int64_t pool_rows, void* k_pool,
+                                void* v_pool, void* stream);
+
+/*
+ * ea_hybrid_attn_decode over a pooled cache: the same outputs (O and LSE of position
+ * seqlens[b] - 1 of every query head) with keys read from the regions above.  A region that
+ * cannot serve its query (outside the pool, over 2^31 bytes, a linear region shorter than
+ * the sequence, a ring shorter than sink + window) gives NaN outputs for that KV head's
+ * query heads and is not read; lengths outside [1, max_seqlen] give NaN for the sequence.
+ * Workspace: ea_decode_workspace_size(batch, max_seqlen, n_heads_q, head_dim) bytes,
+ * 256-byte aligned.  Other arguments as for ea_hybrid_attn_decode.
+ */
+ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const void* v_pool,
+                                     void* o, ea_dtype dt, const int32_t* seqlens,
+                                     const int32_t* seqlens_host, int32_t batch,
+                                     int32_t max_seqlen, int32_t n_heads_q, int32_t n_heads_kv,
+                                     int32_t head_dim, const int64_t* region_base,
+                                     const int32_t* region_rows, int64_t pool_rows,
+                                     const uint8_t* route, int32_t sink, int32_t window,
+                                     float scale, float* lse_out, void* workspace,
+                                     size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -178,3 +178,95 @@ def test_decode_host_seqlens_checks():
     assert decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
     bad = (ctypes.c_int32 * 2)(4097, 17)
     assert decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
+
+
+# ---- pooled decode cache
+
+def test_pool_layout():
+    """Linear regions of `capacity` rows for KV heads with a full query head, sink + window
+    rows for all-sparse ones, packed in (sequence, KV head) order."""
+    import numpy as np
+    route = np.array([[1, 1, 0, 1, 1, 1],
+                      [1, 1, 1, 1, 1, 1],
+                      [0, 0, 0, 0, 0, 0]], dtype=np.uint8)   # 3 sequences, 6 q heads, 3 KV heads
+    base, rows, total = ea.decode_pool_layout(route, 3, capacity=1000, sink=4, window=60)
+    want_rows = [64, 1000, 64, 64, 64, 64, 1000, 1000, 1000]
+    assert rows.tolist() == want_rows
+    assert base.tolist() == [sum(want_rows[:i]) for i in range(9)]
+    assert total == sum(want_rows)
+    # a ring longer than the capacity is still sink + window rows (its slot rule needs them)
+    _, rows, _ = ea.decode_pool_layout(np.ones((1, 2), np.uint8), 1, capacity=10, sink=4, window=60)
+    assert rows.tolist() == [64]
+
+
+def test_pool_layout_rejects():
+    import numpy as np
+    r = np.ones((2, 4), np.uint8)
+    for kw in (dict(capacity=0), dict(window=0), dict(sink=-1)):
+        args = dict(capacity=100, sink=4, window=16)
+        args.update(kw)
+        with pytest.raises(ea.EAError):
+            ea.decode_pool_layout(r, 2, **args)
+    with pytest.raises(ea.EAError):
+        ea.decode_pool_layout(r, 3, capacity=100, sink=4, window=16)  # 4 q heads, 3 KV heads
+
+
+def pool_decode_call(**kw):
+    args = dict(q=FAKE, kp=FAKE + 0x100000, vp=FAKE + 0x200000, o=FAKE + 0x10000,
+                dt=ea.EA_BF16, seqlens=FAKE, seqlens_host=None, batch=2, max_seqlen=4096,
+                hq=32, hkv=8, d=128, rbase=FAKE, rrows=FAKE, pool_rows=2048, route=FAKE,
+                sink=128, window=1024, scale=0.0, lse=None, ws=0x40000000, ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return ea.lib().ea_hybrid_attn_decode_pool(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.EA_ERR_INVALID_ARG),
+    (dict(rbase=None), ea.EA_ERR_INVALID_ARG),
+    (dict(rrows=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dt=5), ea.EA_ERR_INVALID_ARG),
+    (dict(batch=0), ea.EA_ERR_INVALID_ARG),
+    (dict(max_seqlen=0), ea.EA_ERR_INVALID_ARG),
+    (dict(pool_rows=0), ea.EA_ERR_INVALID_ARG),
+    (dict(hq=30), ea.EA_ERR_INVALID_ARG),
+    (dict(hq=72), ea.EA_ERR_UNSUPPORTED),
+    (dict(d=96), ea.EA_ERR_UNSUPPORTED),
+    (dict(window=0), ea.EA_ERR_INVALID_ARG),
+    (dict(sink=-1), ea.EA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ea.EA_ERR_INVALID_ARG),
+    (dict(kp=FAKE + 0x100008), ea.EA_ERR_INVALID_ARG),    # misaligned pool
+    (dict(vp=FAKE + 0x100000), ea.EA_ERR_INVALID_ARG),    # pools overlap
+    (dict(o=FAKE + 0x100000), ea.EA_ERR_INVALID_ARG),     # o overlaps the K pool
+    (dict(ws=0x40000010), ea.EA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), ea.EA_ERR_WORKSPACE),
+])
+def test_pool_decode_rejects(kw, status):
+    assert pool_decode_call(**kw) == status
+    assert ea.last_error()
+
+
+def test_pool_decode_host_seqlens_checks():
+    bad = (ctypes.c_int32 * 2)(0, 17)
+    assert pool_decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
+    bad = (ctypes.c_int32 * 2)(4097, 17)
+    assert pool_decode_call(seqlens_host=bad) == ea.EA_ERR_INVALID_ARG
+
+
+def test_pool_writers_reject():
+    L = ea.lib()
+    fill = dict(k=FAKE, v=FAKE + 0x1000, dt=ea.EA_BF16, cu=FAKE, batch=2, max_seqlen=64, hq=8,
+                hkv=2, d=128, route=FAKE, sink=4, window=16, rbase=FAKE, rrows=FAKE,
+                pool_rows=100, kp=FAKE + 0x100000, vp=FAKE + 0x200000, stream=None)
+    for kw in (dict(k=None), dict(cu=None), dict(max_seqlen=0), dict(d=32), dict(hq=7),
+               dict(pool_rows=0), dict(k=FAKE + 4), dict(vp=FAKE + 0x100010)):
+        a = dict(fill)
+        a.update(kw)
+        assert L.ea_decode_pool_fill(*a.values()) != ea.EA_OK, kw
+    app = dict(k=FAKE, v=FAKE + 0x1000, dt=ea.EA_BF16, pos=FAKE, batch=2, hq=8, hkv=2, d=128,
+               route=FAKE, sink=4, window=16, rbase=FAKE, rrows=FAKE, pool_rows=100,
+               kp=FAKE + 0x100000, vp=FAKE + 0x200000, stream=None)
+    for kw in (dict(pos=None), dict(batch=0), dict(window=0), dict(dt=3), dict(v=FAKE + 8)):
+        a = dict(app)
+        a.update(kw)
+        assert L.ea_decode_pool_append(*a.values()) != ea.EA_OK, kw
