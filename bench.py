@@ -17,7 +17,9 @@ With --mode decode it instead times one decode step of the same routed attention
 (ea_hybrid_attn_decode: every sequence's newest token against its KV cache) on 16 sequences
 of 32K cached tokens, priced against HBM bandwidth: the bytes are the K and V cache rows each
 KV-head group must see (all rows if any of its query heads is full, else sink and window),
-plus q and o.
+plus q and o.  --mode decode_pool times the same step over the pooled cache (KV heads whose
+query heads are all sparse keep only a sink + ring buffer of sink + window rows) and reports
+its size next to the dense cache's.
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
 METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
 DECODE_METRIC = "hybrid-attn decode step: cache GB/s (% HBM peak), 16 x 32K"
+DECODE_POOL_METRIC = "hybrid-attn decode step, pooled sink+ring cache: cache GB/s (% HBM peak), 16 x 32K"
 GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
 ATTN_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_qwen3_8b_32k_traffic.json")
@@ -220,6 +223,41 @@ class DecodeStep:
                               self.route, w.sink, w.window, self.ws)
 
 
+class DecodePoolStep(DecodeStep):
+    """The same step over a pooled cache: linear regions for KV heads with a full query
+    head, sink + ring regions of sink + window rows for all-sparse ones, filled from the
+    dense cache's contents."""
+
+    def __init__(self, name: str):
+        super().__init__(name)
+        w = self.w
+        dev = torch.device("cuda:0")
+        route_cpu = self.cpu[3]
+        base, rows, total = ea.decode_pool_layout(route_cpu.numpy(), w.n_heads_kv, w.capacity,
+                                                  w.sink, w.window)
+        self.pool_rows = total
+        self.kp = torch.empty(total, w.head_dim, dtype=self.q.dtype, device=dev)
+        self.vp = torch.empty_like(self.kp)
+        self.rbase, self.rrows = base.to(dev), rows.to(dev)
+        k = torch.cat([self.kc[b, :L] for b, L in enumerate(self.lens)])
+        v = torch.cat([self.vc[b, :L] for b, L in enumerate(self.lens)])
+        cu = inputs.cu_seqlens(self.lens).to(dev)
+        ea.decode_pool_fill(k, v, cu, self.max_len, w.n_heads_q, self.route, w.sink, w.window,
+                            self.rbase, self.rrows, self.kp, self.vp)
+        torch.cuda.synchronize()
+        del k, v
+        self.dense_cache_bytes = 2 * self.kc.numel() * self.elt
+        self.pool_bytes = 2 * self.kp.numel() * self.elt
+        self.kc = self.vc = None  # the step reads only the pool
+        torch.cuda.empty_cache()
+
+    def step(self):
+        w = self.w
+        ea.hybrid_attn_decode_pool(self.q, self.kp, self.vp, self.o, self.sl, self.max_len,
+                                   w.n_heads_kv, self.rbase, self.rrows, self.route, w.sink,
+                                   w.window, self.ws)
+
+
 def decode_cpu_baseline(st: DecodeStep, seconds: float):
     """fp64 oracle decode of whole sequences of the same batch, one at a time and cycling
     through the batch until `seconds` of work, all cores."""
@@ -243,8 +281,8 @@ def decode_cpu_baseline(st: DecodeStep, seconds: float):
                       f"sequences of the same step ({t_used:.1f} s of fp64 oracle work)"}
 
 
-def decode_main(args):
-    st = DecodeStep(args.workload)
+def decode_main(args, pooled=False):
+    st = DecodePoolStep(args.workload) if pooled else DecodeStep(args.workload)
     w = st.w
     log(f"decode workload {w.name}: B={len(st.lens)} lens={st.lens[:4]}... "
         f"sparse heads {int(st.route.sum().item())} of {st.route.numel()}")
@@ -261,7 +299,7 @@ def decode_main(args):
     G = w.n_heads_q // w.n_heads_kv
     groups_sparse = int(r.view(len(st.lens), w.n_heads_kv, G).all(dim=2).sum().item())
     rec = {
-        "metric": DECODE_METRIC,
+        "metric": DECODE_POOL_METRIC if pooled else DECODE_METRIC,
         "value": round(gbps, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -277,15 +315,20 @@ def decode_main(args):
                    "n_heads_q": w.n_heads_q, "n_heads_kv": w.n_heads_kv,
                    "head_dim": w.head_dim, "sink": w.sink, "window": w.window,
                    "sparse_heads": int(r.sum().item()), "all_sparse_kv_groups": groups_sparse,
-                   "routing": f"bernoulli({w.p_sparse})"},
+                   "routing": f"bernoulli({w.p_sparse})",
+                   "cache": "pooled sink+ring" if pooled else "dense [B, cap, Hkv, D]"},
         "pct_hbm_peak": round(100.0 * gbps / peak, 2),
         "roofline": {"bound": "hbm",
                      "kernel": "decode_split_bf16_kernel<128,4> + decode_combine_kernel",
                      "achieved": round(gbps, 1), "peak": peak, "unit": "GB/s",
                      "frac": round(gbps / peak, 4),
-                     "traffic": measured_traffic(w.name, DECODE_TRAFFIC_FILE, DECODE_SOURCE),
+                     "traffic": None if pooled else measured_traffic(w.name, DECODE_TRAFFIC_FILE,
+                                                                     DECODE_SOURCE),
                      "algorithmic_bytes": st.bytes, "launch_ms": round(ms, 5)},
     }
+    if pooled:
+        rec["cache_bytes"] = {"pooled": st.pool_bytes, "dense": st.dense_cache_bytes,
+                              "ratio": round(st.pool_bytes / st.dense_cache_bytes, 4)}
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:
@@ -299,7 +342,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", choices=("prefill", "decode"), default="prefill")
+    ap.add_argument("--mode", choices=("prefill", "decode", "decode_pool"), default="prefill")
     ap.add_argument("--workload", default=None,
                     help="default qwen3_8b_32k (prefill) or decode_qwen3_8b_32k (decode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -317,9 +360,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
     ea.lib()  # fail loudly if the HIP library is missing
-    if args.mode == "decode":
+    if args.mode in ("decode", "decode_pool"):
         args.workload = args.workload or "decode_qwen3_8b_32k"
-        decode_main(args)
+        decode_main(args, pooled=args.mode == "decode_pool")
         return
     args.workload = args.workload or "qwen3_8b_32k"
 
