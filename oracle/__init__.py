@@ -53,7 +53,7 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        lib.oracle_attn.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, P, i32, i32, dbl,
+        lib.oracle_attn.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, P, i32, i32, dbl,
                                     P, i64, P, P, i32]
         lib.oracle_attn.restype = i32
         lib.oracle_decode.argtypes = [P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
@@ -61,7 +61,7 @@ def _load():
         lib.oracle_decode.restype = i32
         lib.oracle_route.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P]
         lib.oracle_route.restype = i32
-        lib.oracle_worklist.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, i64,
+        lib.oracle_worklist.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, i64,
                                         ctypes.POINTER(i64)]
         lib.oracle_worklist.restype = i32
         lib.oracle_max_threads.argtypes = []
@@ -108,10 +108,12 @@ def max_threads() -> int:
 
 
 def attn(q, k, v, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window, scale=None,
-         rows=None, nthreads=0):
+         rows=None, nthreads=0, cu_seqlens_k=None):
     """fp64 routed attention.  q [T, Hq, D], k/v [T, Hkv, D] (bf16, fp32 or fp64; all
     three the same dtype), cu_seqlens [B+1], route [B, Hq] (0 full, 1 sparse).
     rows: packed token indices to evaluate (None = all).
+    cu_seqlens_k: packing of k/v [Tk, Hkv, D] for a chunked prefill over a KV prefix (each
+    sequence's Lq queries are its last Lq of Lk positions); None = cu_seqlens.
     Returns (o [n_rows, Hq, D] float64, lse [n_rows, Hq] float64)."""
     lib = _load()
     qa, dt = _as_elements(q)
@@ -132,8 +134,12 @@ def attn(q, k, v, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window, scale=
         n_rows = int(rows_arr.shape[0])
     o = np.empty((n_rows, n_heads_q, d), dtype=np.float64)
     lse = np.empty((n_rows, n_heads_q), dtype=np.float64)
+    cuk = None if cu_seqlens_k is None else _np(cu_seqlens_k, np.int32)
+    if cuk is not None and cuk.shape != cu.shape:
+        raise ValueError("cu_seqlens_k must have batch + 1 entries")
     rc = lib.oracle_attn(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
-                         cu.ctypes.data, batch, n_heads_q, n_heads_kv, d,
+                         cu.ctypes.data, None if cuk is None else cuk.ctypes.data,
+                         batch, n_heads_q, n_heads_kv, d,
                          r.ctypes.data, int(sink), int(window), float(scale),
                          None if rows_arr is None else rows_arr.ctypes.data, n_rows,
                          o.ctypes.data, lse.ctypes.data, int(nthreads))
@@ -193,19 +199,22 @@ def route(key_states, cu_seqlens, w1, b1, w2, b2):
     return pooled, logits, r
 
 
-def worklist(route, cu_seqlens, n_heads_q, sink, window, bm, bn):
-    """Sorted work items int32 [N, 4] = (seq, head, q_tile, cost)."""
+def worklist(route, cu_seqlens, n_heads_q, sink, window, bm, bn, cu_seqlens_k=None):
+    """Sorted work items int32 [N, 4] = (seq, head, q_tile, cost).  cu_seqlens_k as for
+    attn (chunk rows at positions Lk - Lq ...)."""
     lib = _load()
     cu = _np(cu_seqlens, np.int32)
     batch = int(cu.shape[0] - 1)
+    cuk = None if cu_seqlens_k is None else _np(cu_seqlens_k, np.int32)
+    cukp = None if cuk is None else cuk.ctypes.data
     r = _np(route, np.uint8).reshape(batch, n_heads_q)
     n = ctypes.c_int64(0)
-    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, batch, n_heads_q, int(sink),
+    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, cukp, batch, n_heads_q, int(sink),
                              int(window), int(bm), int(bn), None, 0, ctypes.byref(n))
     if rc != 0:
         raise ValueError(f"oracle_worklist failed with code {rc}")
     items = np.empty((max(n.value, 1), 4), dtype=np.int32)
-    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, batch, n_heads_q, int(sink),
+    rc = lib.oracle_worklist(r.ctypes.data, cu.ctypes.data, cukp, batch, n_heads_q, int(sink),
                              int(window), int(bm), int(bn), items.ctypes.data, n.value,
                              ctypes.byref(n))
     if rc != 0:

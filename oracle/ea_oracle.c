@@ -77,23 +77,29 @@ static int seq_of_token(const int32_t* cu, int batch, int64_t t) {
  *   x_j = scale * <q_i, k_j> for visible j,  m = max_j x_j,
  *   p_j = exp(x_j - m) / sum_j exp(x_j - m),  o_i = sum_j p_j v_j,  lse_i = m + log(sum).
  * Layouts (token-major, packed by cu_seqlens): q/o [T, hq, d], k/v [T, hkv, d].
+ * cu_k (nullable): a separate packing of k/v [Tk, hkv, d] for a chunked prefill over a KV
+ * prefix.  Sequence b then has Lk = cu_k[b+1] - cu_k[b] keys and Lq = cu_seqlens[b+1] -
+ * cu_seqlens[b] <= Lk queries, the last Lq positions: query row r of the chunk sits at
+ * position i = Lk - Lq + r.  NULL: cu_k = cu_seqlens (a plain prefill, i = r).
  * rows: packed token indices to evaluate (NULL = every token 0..T-1, n_rows = T).
  * o_out [n_rows, hq, d] and lse_out [n_rows, hq] (nullable) are doubles.
  * Returns 0, or -1 on bad arguments.
  */
 int oracle_attn(const void* q, const void* k, const void* v, int dtype,
-                const int32_t* cu_seqlens, int batch, int hq, int hkv, int d,
+                const int32_t* cu_seqlens, const int32_t* cu_k, int batch, int hq, int hkv, int d,
                 const uint8_t* route, int sink, int window, double scale,
                 const int64_t* rows, int64_t n_rows,
                 double* o_out, double* lse_out, int nthreads) {
   if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 || window < 1 || sink < 0)
     return -1;
   const int group = hq / hkv;
+  if (cu_k == NULL) cu_k = cu_seqlens;
   int64_t max_len = 0;
   for (int b = 0; b < batch; ++b) {
-    int64_t len = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
-    if (len < 0) return -1;
-    if (len > max_len) max_len = len;
+    const int64_t len = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
+    const int64_t len_k = (int64_t)cu_k[b + 1] - cu_k[b];
+    if (len < 0 || len_k < len) return -1;
+    if (len_k > max_len) max_len = len_k;
   }
   const int64_t total = cu_seqlens[batch];
   if (rows == NULL) n_rows = total;
@@ -116,8 +122,10 @@ int oracle_attn(const void* q, const void* k, const void* v, int dtype,
       const int h = (int)(task % hq);
       const int64_t t = rows ? rows[r] : r;
       const int b = seq_of_token(cu_seqlens, batch, t);
-      const int64_t start = cu_seqlens[b];
-      const int64_t i = t - start;               /* position of the query in its sequence */
+      const int64_t start = cu_k[b];             /* the sequence's first key */
+      /* position of the query: the chunk holds the last Lq of the sequence's Lk positions */
+      const int64_t i = (int64_t)(cu_k[b + 1] - cu_k[b]) - (cu_seqlens[b + 1] - cu_seqlens[b]) +
+                        (t - cu_seqlens[b]);
       const int g = h / group;                   /* KV head read by query head h */
       const int sparse = route[(int64_t)b * hq + h] != 0;
 
@@ -305,18 +313,22 @@ static int item_order(const void* pa, const void* pb) {
  * metadata; here that metadata is one item per (sequence, query head, BM-row q-tile)
  * with its key-tile cost.  items_out [n, 4] int32 = {seq, head, q_tile, cost}, in the
  * order above.  *n_out receives the item count; items_out may be NULL to only count.
- * capacity bounds the number of items written.
+ * capacity bounds the number of items written.  cu_k (nullable) as for oracle_attn: the
+ * q-tiles cover the chunk's Lq rows, whose positions start at Lk - Lq.
  */
-int oracle_worklist(const uint8_t* route, const int32_t* cu_seqlens, int batch, int hq,
+int oracle_worklist(const uint8_t* route, const int32_t* cu_seqlens, const int32_t* cu_k,
+                    int batch, int hq,
                     int sink, int window, int bm, int bn,
                     int32_t* items_out, int64_t capacity, int64_t* n_out) {
   if (batch < 1 || hq < 1 || bm < 1 || bn < 1 || window < 1 || sink < 0) return -1;
+  if (cu_k == NULL) cu_k = cu_seqlens;
   int64_t n = 0, max_len = 0;
   for (int b = 0; b < batch; ++b) {
     const int64_t len = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
-    if (len < 0) return -1;
+    const int64_t len_k = (int64_t)cu_k[b + 1] - cu_k[b];
+    if (len < 0 || len_k < len) return -1;
     n += (int64_t)hq * ((len + bm - 1) / bm);
-    if (len > max_len) max_len = len;
+    if (len_k > max_len) max_len = len_k;
   }
   *n_out = n;
   if (items_out == NULL) return 0;
@@ -328,6 +340,7 @@ int oracle_worklist(const uint8_t* route, const int32_t* cu_seqlens, int batch, 
   int64_t at = 0;
   for (int b = 0; b < batch; ++b) {
     const int64_t len = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
+    const int64_t off = (int64_t)cu_k[b + 1] - cu_k[b] - len;  /* position of chunk row 0 */
     const int64_t n_q = (len + bm - 1) / bm;
     for (int h = 0; h < hq; ++h) {
       const int sparse = route[(int64_t)b * hq + h] != 0;
@@ -336,7 +349,8 @@ int oracle_worklist(const uint8_t* route, const int32_t* cu_seqlens, int batch, 
         items[at].seq = b;
         items[at].head = h;
         items[at].q_tile = (int32_t)qt;
-        items[at].cost = (int32_t)touched_tiles(m0, m1, sparse, sink, window, bn, cover, n_tiles);
+        items[at].cost =
+            (int32_t)touched_tiles(off + m0, off + m1, sparse, sink, window, bn, cover, n_tiles);
         ++at;
       }
     }

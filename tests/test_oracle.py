@@ -462,3 +462,95 @@ def test_decode_rejects_bad_arguments():
             oracle.decode(q, kc, vc, lens, 1, [[0, 0]], 0, 2)
     with pytest.raises(ValueError):
         oracle.decode(q, kc, vc, [3], 1, [[0, 0]], 0, 0)
+
+
+# ---- chunked prefill over a KV prefix (each sequence's Lq queries are its last Lq of Lk
+# positions; keys and values packed separately)
+
+def chunk_case(lens_k, lens_q, hq, hkv, d, seed):
+    """Full-sequence q/k/v per sequence; the chunk's queries are the last Lq positions."""
+    g = np.random.default_rng(seed)
+    cu_k = np.cumsum([0] + list(lens_k)).astype(np.int32)
+    cu_q = np.cumsum([0] + list(lens_q)).astype(np.int32)
+    qfull = g.standard_normal((int(cu_k[-1]), hq, d))
+    k = g.standard_normal((int(cu_k[-1]), hkv, d))
+    v = g.standard_normal((int(cu_k[-1]), hkv, d))
+    q = np.concatenate([qfull[cu_k[b + 1] - lq:cu_k[b + 1]] for b, lq in enumerate(lens_q)])
+    return qfull, q, k, v, cu_q, cu_k
+
+
+def test_chunked_matches_sdpa_last_rows():
+    """Chunk rows = the last Lq rows of torch SDPA over the whole sequence (library masks),
+    ragged GQA batch, mixed routing, chunks from 1 row to the whole sequence."""
+    lens_k, lens_q = [40, 97, 130, 64], [40, 13, 1, 33]
+    hq, hkv, d, sink, window = 4, 2, 16, 3, 20
+    qfull, q, k, v, cu_q, cu_k = chunk_case(lens_k, lens_q, hq, hkv, d, 5)
+    route = np.array([[0, 1, 1, 0], [1, 1, 1, 1], [1, 0, 1, 1], [0, 0, 1, 1]], np.uint8)
+    scale = 1 / math.sqrt(d)
+    o, lse = oracle.attn(q, k, v, cu_q, hq, hkv, route, sink, window, cu_seqlens_k=cu_k)
+    ro, rl = sdpa_reference(qfull, k, v, cu_k, route, sink, window, scale)
+    for b in range(4):
+        want = slice(int(cu_k[b + 1]) - lens_q[b], int(cu_k[b + 1]))
+        got = slice(int(cu_q[b]), int(cu_q[b + 1]))
+        assert np.abs(o[got] - ro[want]).max() < 1e-12
+        assert np.abs(lse[got] - rl[want]).max() < 1e-12
+
+
+def test_chunked_single_row_is_decode():
+    """A one-row chunk is a decode step over the same history."""
+    lens_k = [1, 50, 300]
+    hq, hkv, d, sink, window = 4, 2, 32, 4, 64
+    _, q, k, v, cu_q, cu_k = chunk_case(lens_k, [1, 1, 1], hq, hkv, d, 9)
+    route = np.array([[1, 1, 0, 1], [1, 1, 1, 1], [0, 1, 1, 1]], np.uint8)
+    o, lse = oracle.attn(q, k, v, cu_q, hq, hkv, route, sink, window, cu_seqlens_k=cu_k)
+    cap = max(lens_k)
+    kc = np.zeros((3, cap, hkv, d))
+    vc = np.zeros((3, cap, hkv, d))
+    for b, L in enumerate(lens_k):
+        kc[b, :L] = k[cu_k[b]:cu_k[b + 1]]
+        vc[b, :L] = v[cu_k[b]:cu_k[b + 1]]
+    od, ld = oracle.decode(q, kc, vc, lens_k, hkv, route, sink, window)
+    assert np.abs(o - od).max() < 1e-12 and np.abs(lse - ld).max() < 1e-12
+
+
+def test_chunks_compose_to_the_prefill():
+    """Cutting a sequence into chunks (each over its full prefix) gives the prefill's rows."""
+    L, hq, hkv, d, sink, window = 150, 2, 1, 16, 5, 30
+    qfull, _, k, v, _, _ = chunk_case([L], [L], hq, hkv, d, 21)
+    route = np.array([[0, 1]], np.uint8)
+    full, _ = oracle.attn(qfull, k, v, [0, L], hq, hkv, route, sink, window)
+    at = 0
+    for c in (1, 63, 64, 22):
+        o, _ = oracle.attn(qfull[at:at + c], k[:at + c], v[:at + c], [0, c], hq, hkv, route,
+                           sink, window, cu_seqlens_k=[0, at + c])
+        assert np.abs(o - full[at:at + c]).max() < 1e-12
+        at += c
+    assert at == L
+
+
+@pytest.mark.parametrize("lk,lq,sink,window,bm,bn", [(300, 300, 5, 40, 64, 32),
+                                                    (300, 77, 5, 40, 64, 32),
+                                                    (1000, 1, 16, 100, 256, 64),
+                                                    (2500, 600, 128, 2048, 256, 64)])
+def test_chunked_worklist_costs_bruteforce(lk, lq, sink, window, bm, bn):
+    """Costs of chunk q-tiles = key tiles with a visible pair for the tile's rows, counted
+    by brute force on the library mask's rows Lk - Lq + [m0, m1)."""
+    route = [[0, 1]]
+    items = oracle.worklist(route, [0, lq], 2, sink, window, bm, bn, cu_seqlens_k=[0, lk])
+    got = {(int(h), int(q)): int(c) for s, h, q, c in items}
+    assert len(got) == 2 * -(-lq // bm)
+    off = lk - lq
+    for h in range(2):
+        m = lib_mask(lk, bool(route[0][h]), sink, window)
+        for qt in range(-(-lq // bm)):
+            rows = m[off + qt * bm:off + min((qt + 1) * bm, lq)]
+            want = sum(bool(rows[:, t * bn:(t + 1) * bn].any()) for t in range(-(-lk // bn)))
+            assert got[(h, qt)] == want
+
+
+def test_chunked_rejects_short_key_sequences():
+    _, q, k, v, cu_q, _ = chunk_case([10], [10], 2, 1, 8, 1)
+    with pytest.raises(ValueError):
+        oracle.attn(q, k, v, cu_q, 2, 1, [[0, 1]], 2, 4, cu_seqlens_k=[0, 9])
+    with pytest.raises(ValueError):
+        oracle.worklist([[0, 1]], [0, 10], 2, 2, 4, 64, 32, cu_seqlens_k=[0, 9])
