@@ -126,10 +126,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 ea_status enqueue_plan(const uint8_t* route, const int32_t* cu, int32_t batch,
                        int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
                        int bm, int bn, int4* items, int32_t* n_items_out, const WsLayout& L,
-                       char* ws, hipStream_t stream) {
-  PlanArgs p;
+                       char* ws, hipStream_t stream, const int32_t* cu_k = nullptr) {
+  PlanArgs p{};
   p.route = route;
   p.cu = cu;
+  p.cu_k = cu_k;
   p.batch = batch;
   p.n_heads_q = n_heads_q;
   p.sink = sink;
@@ -148,13 +149,15 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
                        const int32_t* cu, int32_t batch, int32_t n_heads_q, int32_t n_heads_kv,
                        int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window,
                        float scale, float* lse, const int4* items, const int32_t* n_items,
-                       int64_t item_cap, int32_t* queue, int grid_blocks, hipStream_t stream) {
-  AttnArgs a;
+                       int64_t item_cap, int32_t* queue, int grid_blocks, hipStream_t stream,
+                       const int32_t* cu_k = nullptr) {
+  AttnArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = o;
   a.cu = cu;
+  a.cu_k = cu_k;
   a.route = route;
   a.items = items;
   a.n_items = n_items;
@@ -344,6 +347,60 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
   const int64_t cap = worklist_out ? worklist_capacity : L.item_cap;
   return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
                       sink, window, scale, lse_out, items, counters, cap, counters + 1, 0, st);
+}
+
+ea_status ea_hybrid_attn_prefill_chunked(
+    const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_q_host,
+    const int32_t* cu_seqlens_k_host, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, const uint8_t* route, int32_t sink,
+    int32_t window, float scale, float* lse_out, int32_t* worklist_out,
+    int64_t worklist_capacity, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!cu_seqlens_k) return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (max_seqlen_q < 0 || max_seqlen_q > max_seqlen_k)
+    return fail(EA_ERR_INVALID_ARG, "need 0 <= max_seqlen_q <= max_seqlen_k");
+  int bm = 0, bn = 0;
+  // key windows are sized by max_seqlen_k (also the conservative bound for the planner)
+  ea_status s = check_attn_args(q, k, v, o, dt, cu_seqlens_q, batch, max_seqlen_k, n_heads_q,
+                                n_heads_kv, head_dim, route, sink, window, scale, workspace,
+                                &bm, &bn);
+  if (s != EA_OK) return s;
+  if (o == k || o == v || q == k) return fail(EA_ERR_INVALID_ARG, "o aliases q, k or v");
+  if (worklist_out && worklist_capacity < item_bound(batch, max_seqlen_q, n_heads_q, bm))
+    return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen_q / bm)");
+  if ((cu_seqlens_q_host == nullptr) != (cu_seqlens_k_host == nullptr))
+    return fail(EA_ERR_INVALID_ARG, "give both host copies of the packings or neither");
+  if (cu_seqlens_q_host) {
+    s = check_cu_host(cu_seqlens_q_host, batch, max_seqlen_q);
+    if (s != EA_OK) return s;
+    s = check_cu_host(cu_seqlens_k_host, batch, max_seqlen_k);
+    if (s != EA_OK) return s;
+    for (int32_t b = 0; b < batch; ++b)
+      if (cu_seqlens_k_host[b + 1] - cu_seqlens_k_host[b] <
+          cu_seqlens_q_host[b + 1] - cu_seqlens_q_host[b])
+        return fail(EA_ERR_INVALID_ARG, "a chunk is longer than its key sequence");
+    const size_t elem = dt == EA_BF16 ? 2 : 4;
+    const size_t nq = (size_t)cu_seqlens_q_host[batch] * n_heads_q * head_dim * elem;
+    const size_t nkv = (size_t)cu_seqlens_k_host[batch] * n_heads_kv * head_dim * elem;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+      return fail(EA_ERR_INVALID_ARG, "o overlaps q, k or v");
+  }
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen_q, n_heads_q, 0, 0, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  char* ws = (char*)workspace;
+  hipStream_t st = (hipStream_t)stream;
+  int4* items = worklist_out ? (int4*)worklist_out : (int4*)(ws + L.items);
+  int32_t* counters = (int32_t*)(ws + L.counters);
+  s = enqueue_plan(route, cu_seqlens_q, batch, max_seqlen_q, n_heads_q, sink, window, bm, bn,
+                   items, nullptr, L, ws, st, cu_seqlens_k);
+  if (s != EA_OK) return s;
+  const int64_t cap = worklist_out ? worklist_capacity : L.item_cap;
+  return enqueue_attn(q, k, v, o, dt, cu_seqlens_q, batch, n_heads_q, n_heads_kv, head_dim,
+                      route, sink, window, scale, lse_out, items, counters, cap, counters + 1, 0,
+                      st, cu_seqlens_k);
 }
 
 ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,

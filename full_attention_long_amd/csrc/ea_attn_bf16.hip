@@ -139,13 +139,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const int b = uniform(item.x), h = uniform(item.y), qt = uniform(item.z);
     // an item outside this call's sizes is skipped (the test is uniform across the
     // workgroup; the barrier keeps s_item stable until every thread has read it)
-    if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b]) {
+    // (and so is an item of a chunk longer than its key sequence)
+    if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b] ||
+        (a.cu_k && a.cu_k[b + 1] - a.cu_k[b] < a.cu[b + 1] - a.cu[b])) {
       __syncthreads();
       continue;
     }
     const int seq0 = a.cu[b];
     const int len = a.cu[b + 1] - seq0;
-    const int m0 = qt * BM, m1 = min(m0 + BM, len);
+    // keys: the sequence's own packing, or the KV-prefix packing of a chunked prefill, whose
+    // query rows are the last `len` of its len_k positions (row r at position off + r)
+    const int seq0k = a.cu_k ? uniform(a.cu_k[b]) : seq0;
+    const int len_k = a.cu_k ? uniform(a.cu_k[b + 1]) - seq0k : len;
+    const int off = len_k - len;
+    // m0, m1, wr0, wr1 and qi below are positions in the sequence; the item's chunk rows
+    // are [m0 - off, m1 - off)
+    const int m0 = off + qt * BM, m1 = off + min(qt * BM + BM, len);
     const int kvh = h / group;
     const bool sparse = uniform(a.route[(int64_t)b * Hq + h]) != 0;
     Visit vis = make_visit(sparse, m0, m1, a.sink, a.window);
@@ -156,12 +165,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const int wr0 = m0 + row0, wr1 = min(wr0 + 32, m1);  // this wavefront's rows
 
     // buffer windows: this item's Q/O rows of head h; this sequence's K/V of head kvh
-    const int64_t qo_elem = ((int64_t)(seq0 + m0) * Hq + h) * D;
+    const int64_t qo_elem = ((int64_t)(seq0 + qt * BM) * Hq + h) * D;
     const uint32_t qo_bytes = (uint32_t)(m1 - m0 - 1) * q_row_bytes + D * 2;
     const auto qr = make_rsrc((const __bf16*)a.q + qo_elem, qo_bytes);
     const auto orr = make_rsrc((__bf16*)a.o + qo_elem, qo_bytes);
-    const int64_t kv_elem = ((int64_t)seq0 * Hkv + kvh) * D;
-    const uint32_t kv_bytes = (uint32_t)(len - 1) * kv_row_bytes + D * 2;
+    const int64_t kv_elem = ((int64_t)seq0k * Hkv + kvh) * D;
+    const uint32_t kv_bytes = (uint32_t)(len_k - 1) * kv_row_bytes + D * 2;
     const auto kr = make_rsrc((const __bf16*)a.k + kv_elem, kv_bytes);
     const auto vr = make_rsrc((const __bf16*)a.v + kv_elem, kv_bytes);
 
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       }
     if (a.lse && g == 0 && qi < m1) {
       const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      a.lse[(int64_t)h * total_tokens + seq0 + qi] = m_use * a.scale + logf(l_tot);
+      a.lse[(int64_t)h * total_tokens + seq0 + (qi - off)] = m_use * a.scale + logf(l_tot);
     }
     __syncthreads();  // s_item and the LDS tiles are reused by the next item
   }

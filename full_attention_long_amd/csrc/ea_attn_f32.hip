@@ -61,21 +61,29 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     const int b = item.x, h = item.y, qt = item.z;
     // an item outside this call's sizes is skipped (the test is uniform across the
     // workgroup; the barrier keeps s_item stable until every thread has read it)
-    if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b]) {
+    // (and so is an item of a chunk longer than its key sequence)
+    if (b < 0 || b >= a.batch || h < 0 || h >= Hq || qt < 0 || qt * BM >= a.cu[b + 1] - a.cu[b] ||
+        (a.cu_k && a.cu_k[b + 1] - a.cu_k[b] < a.cu[b + 1] - a.cu[b])) {
       __syncthreads();
       continue;
     }
     const int seq0 = a.cu[b];
     const int len = a.cu[b + 1] - seq0;
-    const int m0 = qt * BM, m1 = min(m0 + BM, len);
+    // keys: the sequence's own packing, or the KV-prefix packing of a chunked prefill whose
+    // chunk row r sits at position off + r
+    const int seq0k = a.cu_k ? a.cu_k[b] : seq0;
+    const int len_k = a.cu_k ? a.cu_k[b + 1] - seq0k : len;
+    const int off = len_k - len;
+    const int m0 = off + qt * BM, m1 = off + min(qt * BM + BM, len);  // positions
     const int kvh = h / group;
     const bool sparse = a.route[(int64_t)b * Hq + h] != 0;
     const Visit vis = make_visit(sparse, m0, m1, a.sink, a.window);
-    const int qi = m0 + row;
+    const int qi = m0 + row;       // position of this thread's query
+    const int qrow = qi - off;     // its chunk row
     const bool live = qi < m1;
 
     float q[DP], o[DP];
-    const float* qp = (const float*)a.q + ((int64_t)(seq0 + qi) * Hq + h) * D + part * DP;
+    const float* qp = (const float*)a.q + ((int64_t)(seq0 + qrow) * Hq + h) * D + part * DP;
 #pragma unroll
     for (int e = 0; e < DP; ++e) {
       q[e] = live ? qp[e] : 0.f;
@@ -90,10 +98,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
         const int kr = idx / (D / 4), c4 = idx % (D / 4);
         const int key = kt * BN + kr;
         f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-        if (key < len) {
-          const int64_t off = ((int64_t)(seq0 + key) * Hkv + kvh) * D + c4 * 4;
-          kv = *(const f32x4*)((const float*)a.k + off);
-          vv = *(const f32x4*)((const float*)a.v + off);
+        if (key < len_k) {
+          const int64_t at = ((int64_t)(seq0k + key) * Hkv + kvh) * D + c4 * 4;
+          kv = *(const f32x4*)((const float*)a.k + at);
+          vv = *(const f32x4*)((const float*)a.v + at);
         }
         *(f32x4*)(ks + kr * RS + c4 * 4) = kv;
         *(f32x4*)(vs + kr * RS + c4 * 4) = vv;
@@ -133,13 +141,13 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     }
 
     if (live) {
-      float* op = (float*)a.o + ((int64_t)(seq0 + qi) * Hq + h) * D + part * DP;
+      float* op = (float*)a.o + ((int64_t)(seq0 + qrow) * Hq + h) * D + part * DP;
       const float inv = 1.0f / l_run;
 #pragma unroll
       for (int e = 0; e < DP; ++e) op[e] = o[e] * inv;
       if (a.lse && part == 0) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        a.lse[(int64_t)h * total_tokens + seq0 + qi] = m_use + logf(l_run);
+        a.lse[(int64_t)h * total_tokens + seq0 + qrow] = m_use + logf(l_run);
       }
     }
     __syncthreads();

@@ -50,6 +50,9 @@ hipError_t launch_route(const void* ks, int kdt, int kv_dim, const int32_t* cu, 
 struct PlanArgs {
   const uint8_t* route;
   const int32_t* cu;
+  // nullable: key packing of a chunked prefill over a KV prefix (sequence b's cu[b+1]-cu[b]
+  // queries are the last of its cu_k[b+1]-cu_k[b] positions); null = cu
+  const int32_t* cu_k;
   int batch, n_heads_q, sink, window, bm, bn;
   int4* items;
   int32_t* counters;      // [0] n_items, [1] queue head, [2] workgroups done (both zeroed)
@@ -63,6 +66,7 @@ struct AttnArgs {
   const void* v;
   void* o;
   const int32_t* cu;
+  const int32_t* cu_k;    // nullable, as in PlanArgs
   const uint8_t* route;
   const int4* items;
   const int32_t* n_items;

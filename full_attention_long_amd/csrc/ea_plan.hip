@@ -3,7 +3,9 @@
 // decision to one kernel as metadata so that full and sparse heads share a launch; here
 // that metadata is a list of (sequence, head, q-tile, cost) items in longest-first order.
 //
-// Cost of an item = number of bn-key tiles the kernel visits for its rows [m0, m1):
+// Cost of an item = number of bn-key tiles the kernel visits for its rows [m0, m1) (query
+// positions; in a chunked prefill over a KV prefix the chunk's rows start at position
+// Lk - Lq, and a sequence with Lk < Lq gets no items):
 //   full head:   tiles 0 .. (m1-1)/bn
 //   sparse head: sink tiles 0 .. ceil(min(sink, m1)/bn)-1 united with window tiles
 //                max(0, m0-window+1)/bn .. (m1-1)/bn
@@ -42,7 +44,9 @@ __device__ __forceinline__ int4 make_cell(int i, const PlanArgs& a, const int* q
   }
   const int b = lo, qt = f - qt_prefix[b];
   const int len = a.cu[b + 1] - a.cu[b];
-  const int m0 = qt * a.bm, m1 = min(m0 + a.bm, len);
+  const int off = a.cu_k ? (a.cu_k[b + 1] - a.cu_k[b]) - len : 0;  // position of chunk row 0
+  if (off < 0) return int4{b, qt, 0, 0};  // keys shorter than the chunk: no items
+  const int m0 = off + qt * a.bm, m1 = off + min(qt * a.bm + a.bm, len);
   const int t_hi = (m1 - 1) / a.bn;
   const int n_sink = ceil_div(min(a.sink, m1), a.bn);
   const int t_lo = max(0, m0 - a.window + 1) / a.bn;

@@ -20,7 +20,8 @@ EA_BF16, EA_F32 = 0, 1
 EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_error",
            "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run",
            "ea_decode_workspace_size", "ea_hybrid_attn_decode", "ea_decode_pool_layout",
-           "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool")
+           "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool",
+           "ea_hybrid_attn_prefill_chunked")
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib():
     L.ea_hybrid_attn_decode.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, P,
                                         i32, i32, f32, P, P, sz, P]
     L.ea_hybrid_attn_decode.restype = i32
+    L.ea_hybrid_attn_prefill_chunked.argtypes = [P, P, P, P, i32, P, P, P, P, i32, i32, i32, i32,
+                                                 i32, i32, P, i32, i32, f32, P, P, i64, P, sz,
+                                                 P]
+    L.ea_hybrid_attn_prefill_chunked.restype = i32
     L.ea_decode_pool_layout.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P]
     L.ea_decode_pool_layout.restype = i32
     L.ea_decode_pool_fill.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32, P, P,
@@ -269,3 +274,22 @@ def hybrid_attn_decode_pool(q, k_pool, v_pool, o, seqlens, max_seqlen, n_heads_k
                                             _ptr(lse_out), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _stream(stream)))
+
+
+def hybrid_attn_prefill_chunked(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                max_seqlen_k, route_bits, sink, window, workspace, scale=0.0,
+                                cu_seqlens_q_host=None, cu_seqlens_k_host=None, lse_out=None,
+                                worklist_out=None, stream=None):
+    """ea_hybrid_attn_prefill_chunked: q/o [Tq, Hq, D] (each sequence's last Lq positions),
+    k/v [Tk, Hkv, D] packed by cu_seqlens_k."""
+    batch = cu_seqlens_q.numel() - 1
+    hq = hk = None
+    if cu_seqlens_q_host is not None:
+        hq = (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu_seqlens_q_host])
+        hk = (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu_seqlens_k_host])
+    _check(lib().ea_hybrid_attn_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), hq, hk, batch, max_seqlen_q, max_seqlen_k, q.shape[1], k.shape[1],
+        q.shape[2], _ptr(route_bits), sink, window, float(scale), _ptr(lse_out),
+        _ptr(worklist_out), _capacity(worklist_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -152,6 +152,31 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Chunked prefill over a KV prefix: the same routed attention when each sequence's queries
+ * are only its newest tokens.  Sequence b has Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b]
+ * positions whose keys and values are k, v [Tk, n_heads_kv, head_dim] (an earlier prefix,
+ * e.g. cached, followed by the new chunk), and Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] <= Lk
+ * queries q [Tq, n_heads_q, head_dim], the last Lq positions: query row r of the chunk sits
+ * at position i = Lk - Lq + r and sees, under its head's mode, the keys j <= i visible to
+ * position i exactly as in ea_hybrid_attn_prefill.  o [Tq, n_heads_q, head_dim];
+ * lse_out [n_heads_q, Tq].  With cu_seqlens_k equal to cu_seqlens_q this is
+ * ea_hybrid_attn_prefill.  max_seqlen_q <= max_seqlen_k bound the two packings (per-sequence
+ * key windows need max_seqlen_k * n_heads_kv * head_dim * elem < 2^31).
+ * cu_seqlens_q_host / cu_seqlens_k_host: give both (host copies, checked: monotone, within
+ * the bounds, Lq <= Lk per sequence, o not overlapping q, k, v) or neither.  On the device
+ * a sequence with Lk < Lq gets no work and its output rows are not written.  Other
+ * arguments, the workspace and worklist_out as for ea_hybrid_attn_prefill, with max_seqlen_q
+ * in place of max_seqlen for the work list bound.
+ */
+ea_status ea_hybrid_attn_prefill_chunked(
+    const void* q, const void* k, const void* v, void* o, ea_dtype dt,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_q_host,
+    const int32_t* cu_seqlens_k_host, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, const uint8_t* route, int32_t sink,
+    int32_t window, float scale, float* lse_out, int32_t* worklist_out,
+    int64_t worklist_capacity, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * The attention half of ea_hybrid_attn_prefill on a work list made by ea_build_worklist
  * (same dt, head_dim, sink, window, route and cu_seqlens).  worklist and n_items are
  * device pointers; worklist_capacity is the work list's size in items (the kernels never

@@ -270,3 +270,30 @@ def test_pool_writers_reject():
         a = dict(app)
         a.update(kw)
         assert L.ea_decode_pool_append(*a.values()) != ea.EA_OK, kw
+
+
+def chunked_call(**kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000,
+                dt=ea.EA_BF16, cu_q=FAKE, cu_k=FAKE + 0x100, cu_q_host=None, cu_k_host=None,
+                batch=2, max_q=1024, max_k=4096, hq=32, hkv=8, d=128, route=FAKE, sink=128,
+                window=1024, scale=0.0, lse=None, wl=None, wl_cap=0, ws=0x40000000,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return ea.lib().ea_hybrid_attn_prefill_chunked(*args.values())
+
+
+def test_chunked_prefill_rejects():
+    assert chunked_call(cu_k=None) == ea.EA_ERR_INVALID_ARG
+    assert chunked_call(max_q=5000) == ea.EA_ERR_INVALID_ARG           # beyond max_seqlen_k
+    assert chunked_call(max_q=-1) == ea.EA_ERR_INVALID_ARG
+    assert chunked_call(d=96) == ea.EA_ERR_UNSUPPORTED
+    assert chunked_call(o=FAKE + 0x1000000) == ea.EA_ERR_INVALID_ARG   # o is k
+    assert chunked_call(wl=FAKE, wl_cap=10) == ea.EA_ERR_INVALID_ARG   # work list too short
+    assert chunked_call(ws_bytes=16) == ea.EA_ERR_WORKSPACE
+    q_host = (ctypes.c_int32 * 3)(0, 100, 150)
+    assert chunked_call(cu_q_host=q_host) == ea.EA_ERR_INVALID_ARG     # only one host copy
+    k_host = (ctypes.c_int32 * 3)(0, 90, 300)                          # 100 queries, 90 keys
+    assert chunked_call(cu_q_host=q_host, cu_k_host=k_host) == ea.EA_ERR_INVALID_ARG
+    k_host = (ctypes.c_int32 * 3)(0, 5000, 5100)                       # a key sequence > max_k
+    assert chunked_call(cu_q_host=q_host, cu_k_host=k_host) == ea.EA_ERR_INVALID_ARG
+    assert ea.last_error()
