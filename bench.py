@@ -19,7 +19,8 @@ of 32K cached tokens, priced against HBM bandwidth: the bytes are the K and V ca
 KV-head group must see (all rows if any of its query heads is full, else sink and window),
 plus q and o.  --mode decode_pool times the same step over the pooled cache (KV heads whose
 query heads are all sparse keep only a sink + ring buffer of sink + window rows) and reports
-its size next to the dense cache's.
+its size next to the dense cache's.  --mode prefill_chunk times the router plus a chunked
+prefill of the layer's last 4096 tokens over the other 28672 as a KV prefix.
 """
 from __future__ import annotations
 
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
 METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
+CHUNK_METRIC = "hybrid-attn chunked prefill (4K chunk over a 28K prefix) effective TFLOP/s"
 DECODE_METRIC = "hybrid-attn decode step: cache GB/s (% HBM peak), 16 x 32K"
 DECODE_POOL_METRIC = "hybrid-attn decode step, pooled sink+ring cache: cache GB/s (% HBM peak), 16 x 32K"
 GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
@@ -337,12 +339,68 @@ def decode_main(args, pooled=False):
     print(json.dumps(rec), flush=True)
 
 
+def chunk_main(args):
+    """Router over the layer's key states, then the chunked prefill of the last `chunk`
+    tokens over the rest as a KV prefix (ea_hybrid_attn_prefill_chunked)."""
+    layer = Layer(args.workload)
+    w = layer.w
+    assert len(layer.lens) == 1, "one sequence"
+    Lk = layer.T
+    Lq = min(args.chunk, Lk)
+    dev = torch.device("cuda:0")
+    q = layer.q[Lk - Lq:].contiguous()
+    o = torch.empty_like(q)
+    cu_q = inputs.cu_seqlens([Lq]).to(dev)
+    cu_k = layer.cu
+    layer.do_route()
+    torch.cuda.synchronize()
+
+    def step():
+        layer.do_route()
+        ea.hybrid_attn_prefill_chunked(q, layer.k, layer.v, o, cu_q, cu_k, Lq, Lk, layer.route,
+                                       w.sink, w.window, layer.ws)
+
+    def attn_only():
+        ea.hybrid_attn_prefill_chunked(q, layer.k, layer.v, o, cu_q, cu_k, Lq, Lk, layer.route,
+                                       w.sink, w.window, layer.ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, args.steps)
+    ms_attn = time_events(attn_only, args.steps)
+    r = layer.route.cpu().tolist()
+    F = metrics.chunk_flops([Lk], [Lq], r, w.head_dim, w.sink, w.window)
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
+    value = F / (ms * 1e-3) / 1e12
+    attn_tf = F / (ms_attn * 1e-3) / 1e12
+    rec = {
+        "metric": CHUNK_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + f"_chunk{Lq}", "cached_prefix": Lk - Lq, "chunk": Lq,
+                   "n_heads_q": w.n_heads_q, "n_heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
+                   "sink": w.sink, "window": w.window,
+                   "sparse_heads": int(layer.route.sum().item()), "routing": "router"},
+        "pct_bf16_peak": round(100.0 * value / peak, 2),
+        "effective_tflop": round(F / 1e12, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128>", "achieved": round(attn_tf, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(attn_tf / peak, 4),
+                     "traffic": None, "launch_ms": round(ms_attn, 4),
+                     "note": "launch_ms includes the planner launch"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", choices=("prefill", "decode", "decode_pool"), default="prefill")
+    ap.add_argument("--mode", choices=("prefill", "prefill_chunk", "decode", "decode_pool"),
+                    default="prefill")
+    ap.add_argument("--chunk", type=int, default=4096, help="chunk length for --mode prefill_chunk")
     ap.add_argument("--workload", default=None,
                     help="default qwen3_8b_32k (prefill) or decode_qwen3_8b_32k (decode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -365,6 +423,9 @@ def main():
         decode_main(args, pooled=args.mode == "decode_pool")
         return
     args.workload = args.workload or "qwen3_8b_32k"
+    if args.mode == "prefill_chunk":
+        chunk_main(args)
+        return
 
     layer = Layer(args.workload)
     w = layer.w

@@ -42,6 +42,19 @@ def effective_flops(lengths, route, head_dim: int, sink: int, window: int) -> in
     return total
 
 
+def chunk_flops(lengths_k, lengths_q, route, head_dim: int, sink: int, window: int) -> int:
+    """Effective FLOPs of a chunked prefill: the chunk rows are the last Lq of Lk positions and
+    a row's visible keys depend only on its position, so their pairs are
+    visible_pairs(Lk) - visible_pairs(Lk - Lq)."""
+    total = 0
+    for b, (Lk, Lq) in enumerate(zip(lengths_k, lengths_q)):
+        for r in route[b]:
+            sp = bool(int(r))
+            total += 4 * int(head_dim) * (visible_pairs(Lk, sp, sink, window) -
+                                          visible_pairs(Lk - Lq, sp, sink, window))
+    return total
+
+
 def io_bytes(total_tokens: int, n_heads_q: int, n_heads_kv: int, head_dim: int,
              elem_bytes: int) -> int:
     """Algorithmic HBM bytes of one attention launch: Q, K, V read once, O written once."""

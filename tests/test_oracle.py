@@ -554,3 +554,12 @@ def test_chunked_rejects_short_key_sequences():
         oracle.attn(q, k, v, cu_q, 2, 1, [[0, 1]], 2, 4, cu_seqlens_k=[0, 9])
     with pytest.raises(ValueError):
         oracle.worklist([[0, 1]], [0, 10], 2, 2, 4, 64, 32, cu_seqlens_k=[0, 9])
+
+
+@pytest.mark.parametrize("lk,lq,sink,window", [(100, 100, 3, 20), (100, 1, 3, 20), (257, 60, 0, 7),
+                                               (64, 30, 64, 1)])
+def test_chunk_flops_closed_form(lk, lq, sink, window):
+    """Pairs of the chunk rows = the library mask's rows Lk - Lq .. Lk - 1."""
+    for sparse in (0, 1):
+        want = int(lib_mask(lk, bool(sparse), sink, window)[lk - lq:].sum())
+        assert metrics.chunk_flops([lk], [lq], [[sparse]], 1, sink, window) == 4 * want
