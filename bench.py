@@ -352,17 +352,19 @@ def chunk_main(args):
     o = torch.empty_like(q)
     cu_q = inputs.cu_seqlens([Lq]).to(dev)
     cu_k = layer.cu
+    ws = torch.empty(ea.prefill_chunked_workspace_size(1, Lq, w.n_heads_q, w.head_dim),
+                     dtype=torch.uint8, device=dev)
     layer.do_route()
     torch.cuda.synchronize()
 
     def step():
         layer.do_route()
         ea.hybrid_attn_prefill_chunked(q, layer.k, layer.v, o, cu_q, cu_k, Lq, Lk, layer.route,
-                                       w.sink, w.window, layer.ws)
+                                       w.sink, w.window, ws)
 
     def attn_only():
         ea.hybrid_attn_prefill_chunked(q, layer.k, layer.v, o, cu_q, cu_k, Lq, Lk, layer.route,
-                                       w.sink, w.window, layer.ws)
+                                       w.sink, w.window, ws)
 
     for _ in range(args.warmup):
         step()

@@ -125,9 +125,20 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 ea_status enqueue_plan(const uint8_t* route, const int32_t* cu, int32_t batch,
                        int32_t max_seqlen, int32_t n_heads_q, int32_t sink, int32_t window,
-                       int bm, int bn, int4* items, int32_t* n_items_out, const WsLayout& L,
-                       char* ws, hipStream_t stream, const int32_t* cu_k = nullptr) {
+                       int bm, int bn, int4* items, int64_t item_cap, int32_t* n_items_out,
+                       const WsLayout& L, char* ws, hipStream_t stream,
+                       const int32_t* cu_k = nullptr, int split_workers = 0) {
   PlanArgs p{};
+  // the planner writes nothing past this many items (nor past its LDS cells): device lengths
+  // beyond max_seqlen give an empty work list instead
+  if (split_workers > 0 && item_cap > L.item_cap) item_cap = L.item_cap;
+  p.item_cap = (int32_t)(item_cap < INT32_MAX ? item_cap : INT32_MAX);
+  if (split_workers > 0) {
+    p.split_workers = split_workers;
+    p.piece_prefix = (int32_t*)(ws + L.piece_prefix);
+    p.slot_base = (int32_t*)(ws + L.slot_base);
+    p.split_list = (int32_t*)(ws + L.split_list);
+  }
   p.route = route;
   p.cu = cu;
   p.cu_k = cu_k;
@@ -150,8 +161,16 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
                        int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window,
                        float scale, float* lse, const int4* items, const int32_t* n_items,
                        int64_t item_cap, int32_t* queue, int grid_blocks, hipStream_t stream,
-                       const int32_t* cu_k = nullptr) {
+                       const int32_t* cu_k = nullptr, const WsLayout* split = nullptr,
+                       char* ws = nullptr) {
   AttnArgs a{};
+  if (split) {  // split-KV: pieces from the planner's split phase, then the combine launch
+    a.piece_prefix = (const int32_t*)(ws + split->piece_prefix);
+    a.slot_base = (const int32_t*)(ws + split->slot_base);
+    a.n_pieces = (const int32_t*)(ws + split->counters) + 3;
+    a.o_part = (float*)(ws + split->o_part);
+    a.ml_part = (float*)(ws + split->ml_part);
+  }
   a.q = q;
   a.k = k;
   a.v = v;
@@ -180,6 +199,11 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
   }
   hipError_t e = dt == EA_BF16 ? launch_attn_bf16(a, grid, stream) : launch_attn_f32(a, grid, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (split) {
+    const int32_t* counters = (const int32_t*)(ws + split->counters);
+    e = launch_split_combine(a, (const int32_t*)(ws + split->split_list), counters + 4, stream);
+    if (e != hipSuccess) return hip_fail(e, "split combine launch");
+  }
   return EA_OK;
 }
 
@@ -210,6 +234,22 @@ bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_
   return true;
 }
 
+bool ws_layout_split(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q, int32_t head_dim,
+                     WsLayout* out) {
+  if (head_dim < 1) return false;
+  WsLayout L;
+  if (!ws_layout(batch, max_seqlen_q, n_heads_q, 0, 0, &L)) return false;
+  size_t at = align256(L.total);
+  L.piece_prefix = at;  at = align256(at + sizeof(int32_t) * (size_t)(L.item_cap + 1));
+  L.slot_base = at;     at = align256(at + sizeof(int32_t) * (size_t)L.item_cap);
+  L.split_list = at;    at = align256(at + sizeof(int32_t) * (size_t)kSplitSlots);
+  L.o_part = at;        at = align256(at + sizeof(float) * (size_t)kSplitSlots * kBf16BM * head_dim);
+  L.ml_part = at;       at = align256(at + sizeof(float) * (size_t)kSplitSlots * kBf16BM * 2);
+  L.total = at;
+  *out = L;
+  return true;
+}
+
 }  // namespace ea
 
 using namespace ea;
@@ -220,6 +260,13 @@ size_t ea_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, i
                          int32_t hidden) {
   WsLayout L;
   if (!ws_layout(batch, max_seqlen, n_heads_q, kv_dim, hidden, &L)) return 0;
+  return L.total;
+}
+
+size_t ea_prefill_chunked_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q,
+                                         int32_t head_dim) {
+  WsLayout L;
+  if (!ws_layout_split(batch, max_seqlen_q, n_heads_q, head_dim, &L)) return 0;
   return L.total;
 }
 
@@ -296,7 +343,7 @@ ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn,
-                   (int4*)worklist_out, n_items_out, L, ws, st);
+                   (int4*)worklist_out, worklist_capacity, n_items_out, L, ws, st);
   if (s != EA_OK) return s;
   if (n_items_host) {
     hipError_t e = hipMemcpyAsync(n_items_host, ws + L.counters, sizeof(int32_t),
@@ -341,10 +388,10 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
   hipStream_t st = (hipStream_t)stream;
   int4* items = worklist_out ? (int4*)worklist_out : (int4*)(ws + L.items);
   int32_t* counters = (int32_t*)(ws + L.counters);
-  s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn, items,
-                   nullptr, L, ws, st);
-  if (s != EA_OK) return s;
   const int64_t cap = worklist_out ? worklist_capacity : L.item_cap;
+  s = enqueue_plan(route, cu_seqlens, batch, max_seqlen, n_heads_q, sink, window, bm, bn, items,
+                   cap, nullptr, L, ws, st);
+  if (s != EA_OK) return s;
   return enqueue_attn(q, k, v, o, dt, cu_seqlens, batch, n_heads_q, n_heads_kv, head_dim, route,
                       sink, window, scale, lse_out, items, counters, cap, counters + 1, 0, st);
 }
@@ -386,21 +433,32 @@ ea_status ea_hybrid_attn_prefill_chunked(
     if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
       return fail(EA_ERR_INVALID_ARG, "o overlaps q, k or v");
   }
+  // bf16: long items run split over several workgroups (split-KV); fp32: one per item
+  const bool split = dt == EA_BF16;
   WsLayout L;
-  if (!ws_layout(batch, max_seqlen_q, n_heads_q, 0, 0, &L))
+  if (!(split ? ws_layout_split(batch, max_seqlen_q, n_heads_q, head_dim, &L)
+              : ws_layout(batch, max_seqlen_q, n_heads_q, 0, 0, &L)))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
-  if (ws_bytes < L.total) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_workspace_size()");
+  if (ws_bytes < L.total)
+    return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_prefill_chunked_workspace_size()");
   char* ws = (char*)workspace;
   hipStream_t st = (hipStream_t)stream;
   int4* items = worklist_out ? (int4*)worklist_out : (int4*)(ws + L.items);
   int32_t* counters = (int32_t*)(ws + L.counters);
-  s = enqueue_plan(route, cu_seqlens_q, batch, max_seqlen_q, n_heads_q, sink, window, bm, bn,
-                   items, nullptr, L, ws, st, cu_seqlens_k);
-  if (s != EA_OK) return s;
+  int workers = 0;
+  if (split) {
+    int ncu = 0;
+    const hipError_t e = cu_count(&ncu);
+    if (e != hipSuccess) return hip_fail(e, "device query");
+    workers = ncu * attn_bf16_blocks_per_cu();
+  }
   const int64_t cap = worklist_out ? worklist_capacity : L.item_cap;
+  s = enqueue_plan(route, cu_seqlens_q, batch, max_seqlen_q, n_heads_q, sink, window, bm, bn,
+                   items, cap, nullptr, L, ws, st, cu_seqlens_k, workers);
+  if (s != EA_OK) return s;
   return enqueue_attn(q, k, v, o, dt, cu_seqlens_q, batch, n_heads_q, n_heads_kv, head_dim,
                       route, sink, window, scale, lse_out, items, counters, cap, counters + 1, 0,
-                      st, cu_seqlens_k);
+                      st, cu_seqlens_k, split ? &L : nullptr, ws);
 }
 
 ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,

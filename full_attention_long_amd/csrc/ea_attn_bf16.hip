@@ -72,10 +72,14 @@ struct Shape {
   static __device__ __forceinline__ int swz_v(int r) { return (4 * r) & (CHUNKS - 1) & ~3; }
 };
 
-// Tile-visit plan of one item.  Tiles [0, n1) (sink) then [s2, t_hi] (window or causal).
+// Tile-visit plan of one item.  Tiles [0, n1) (sink) then [s2, t_hi] (window or causal); a
+// piece of a split item visits entries [base, base + count) of that sequence.
 struct Visit {
-  int n1, s2, t_hi, count;
-  __device__ __forceinline__ int tile(int n) const { return n < n1 ? n : s2 + (n - n1); }
+  int n1, s2, t_hi, count, base;
+  __device__ __forceinline__ int tile(int n) const {
+    n += base;
+    return n < n1 ? n : s2 + (n - n1);
+  }
 };
 
 __device__ __forceinline__ Visit make_visit(bool sparse, int m0, int m1, int sink, int window) {
@@ -90,6 +94,7 @@ __device__ __forceinline__ Visit make_visit(bool sparse, int m0, int m1, int sin
     v.s2 = 0;
   }
   v.count = v.n1 + max(0, v.t_hi - v.s2 + 1);
+  v.base = 0;
   return v;
 }
 
@@ -133,8 +138,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     __syncthreads();
     // the item index is uniform: keeping it (and so the item, its tile plan and the
     // buffer offsets) in scalar registers keeps the direct-to-LDS loads' offsets scalar
-    const int it = uniform(s_item);
-    if (it >= n_items) break;
+    int it = uniform(s_item);
+    int piece = 0, n_pieces = 1;
+    if (a.piece_prefix) {
+      // split-KV: the queue hands out pieces; piece `it` belongs to the last item whose first
+      // piece is <= it
+      const int v = it;
+      if (v >= min(*a.n_pieces, a.piece_prefix[n_items])) break;
+      int lo = 0, hi = n_items - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.piece_prefix[mid] <= v) lo = mid; else hi = mid - 1;
+      }
+      it = uniform(lo);
+      piece = uniform(v - a.piece_prefix[it]);
+      n_pieces = uniform(a.piece_prefix[it + 1] - a.piece_prefix[it]);
+    } else if (it >= n_items) {
+      break;
+    }
     const int4 item = a.items[it];
     const int b = uniform(item.x), h = uniform(item.y), qt = uniform(item.z);
     // an item outside this call's sizes is skipped (the test is uniform across the
@@ -161,7 +182,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     vis.n1 = uniform(vis.n1);
     vis.s2 = uniform(vis.s2);
     vis.t_hi = uniform(vis.t_hi);
+    if (n_pieces > 1) {  // this piece's share of the plan (every piece gets >= 1 tile)
+      const int lo_n = piece * vis.count / n_pieces, hi_n = (piece + 1) * vis.count / n_pieces;
+      vis.base = lo_n;
+      vis.count = hi_n - lo_n;
+    }
     vis.count = uniform(vis.count);
+    vis.base = uniform(vis.base);
     const int wr0 = m0 + row0, wr1 = min(wr0 + 32, m1);  // this wavefront's rows
 
     // buffer windows: this item's Q/O rows of head h; this sequence's K/V of head kvh
@@ -440,6 +467,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       slot_end(s);
     }
 
+    // ---- epilogue of a piece of a split item: unnormalised O, the row's reference max and
+    // sum, in fp32, to the piece's slot (merged by the combine kernel)
+    if (n_pieces > 1) {
+      const float l_tot = l_run + xor32(l_run);
+      const int64_t slot = a.slot_base[it] + piece;
+      const int row = row0 + l32;
+      float* op = a.o_part + (slot * BM + row) * D;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 w = {oacc[dt][4 * rq + 0], oacc[dt][4 * rq + 1], oacc[dt][4 * rq + 2],
+                           oacc[dt][4 * rq + 3]};
+          *(f32x4*)(op + 32 * dt + 8 * rq + 4 * g) = w;
+        }
+      if (g == 0) {
+        a.ml_part[(slot * BM + row) * 2 + 0] = m_ref;
+        a.ml_part[(slot * BM + row) * 2 + 1] = l_tot;
+      }
+      __syncthreads();  // s_item and the LDS tiles are reused by the next item
+      continue;
+    }
     // ---- epilogue: O = O / l, round to bf16, store this lane's query row
     const float l_tot = l_run + xor32(l_run);
     const float inv = 1.0f / l_tot;
@@ -467,9 +516,62 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// Merge of a split item's pieces: for each of its rows, M = max of the pieces' reference
+// maxima, w_p = 2^((m_p - M) * scale * log2 e), O = sum_p O_p w_p / sum_p l_p w_p (fp32, one
+// bf16 rounding), LSE = M * scale + ln sum_p l_p w_p.  One workgroup per split item; a thread
+// takes 4 head dimensions of a row.
+template <int D>
+__global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, const int32_t* split_list,
+                                                            const int32_t* n_split) {
+  const int k = blockIdx.x;
+  if (k >= min(*n_split, kSplitSlots)) return;
+  const int it = split_list[k];
+  const int4 item = a.items[it];
+  const int b = item.x, h = item.y, qt = item.z;
+  const int Hq = a.n_heads_q;
+  const int seq0 = a.cu[b];
+  const int len = a.cu[b + 1] - seq0;
+  const int r0 = qt * BM, nrows = min(BM, len - r0);
+  const int ns = a.piece_prefix[it + 1] - a.piece_prefix[it];
+  const int64_t slot0 = a.slot_base[it];
+  const int total_tokens = a.cu[a.batch];
+  const float c_log2 = a.scale * 1.4426950408889634f;
+  constexpr int C4 = D / 4, RPP = 256 / C4;
+  const int c = threadIdx.x % C4;
+  for (int r = threadIdx.x / C4; r < nrows; r += RPP) {
+    float M = -INFINITY;
+    for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ml_part[((slot0 + p) * BM + r) * 2]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float l = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < ns; ++p) {
+      const float m = a.ml_part[((slot0 + p) * BM + r) * 2];
+      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - Mu) * c_log2);
+      l += a.ml_part[((slot0 + p) * BM + r) * 2 + 1] * w;
+      acc += w * *(const f32x4*)(a.o_part + ((slot0 + p) * BM + r) * D + 4 * c);
+    }
+    const float inv = 1.0f / l;
+    __bf16* o = (__bf16*)a.o + ((int64_t)(seq0 + r0 + r) * Hq + h) * D + 4 * c;
+    u32x2 wv;
+    wv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    wv[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)o = wv;
+    if (a.lse && c == 0) a.lse[(int64_t)h * total_tokens + seq0 + r0 + r] = Mu * a.scale + logf(l);
+  }
+}
+
 }  // namespace
 
 int attn_bf16_blocks_per_cu() { return 1; }
+
+hipError_t launch_split_combine(const AttnArgs& a, const int32_t* split_list,
+                                const int32_t* n_split, hipStream_t stream) {
+  if (a.head_dim == 128)
+    split_combine_kernel<128><<<kSplitSlots, 256, 0, stream>>>(a, split_list, n_split);
+  else
+    split_combine_kernel<64><<<kSplitSlots, 256, 0, stream>>>(a, split_list, n_split);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int grid, hipStream_t stream) {
   if (a.head_dim == 128)

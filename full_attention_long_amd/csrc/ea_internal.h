@@ -20,6 +20,12 @@ constexpr int kMinBM = 64;           // smallest q-tile over all paths (sizes th
 constexpr int kPlanMaxCells = 8192;  // 2 cells per (sequence, q-tile)
 constexpr int kPlanMaxBatch = 1024;  // sequences per call
 constexpr int kPlanMaxHeads = 128;   // query heads
+// Split-KV for the bf16 chunked prefill: a work item whose key-tile cost exceeds a budget is
+// run as up to kSplitMaxPieces pieces over consecutive parts of its tile plan, each writing
+// fp32 partial results to one of kSplitSlots slots, merged afterwards.
+constexpr int kSplitMaxPieces = 16;
+constexpr int kSplitSlots = 512;
+constexpr int kSplitMinTiles = 32;   // smallest budget (tiles per piece)
 
 // ---------------------------------------------------------------- workspace
 struct WsLayout {
@@ -29,7 +35,14 @@ struct WsLayout {
   size_t router_x = 0;        // float [batch][kv_dim]   pooled key states
   size_t router_h = 0;        // float [batch][hidden]   SiLU(W1 x + b1)
   size_t items = 0;           // int4 [batch * n_heads_q * qt_max] (internal work list)
-  size_t counters = 0;        // int32 [16]: 0 n_items, 1 queue head, 2 workgroups done
+  size_t counters = 0;        // int32 [16]: 0 n_items, 1 queue head, 2 workgroups done,
+                              // 3 pieces (split-KV), 4 split items
+  // split-KV (only laid out by ws_layout_split)
+  size_t piece_prefix = 0;    // int32 [item_cap + 1]: first piece of every item
+  size_t slot_base = 0;       // int32 [item_cap]: first partial slot of a split item, else -1
+  size_t split_list = 0;      // int32 [kSplitSlots]: the split items
+  size_t o_part = 0;          // float [kSplitSlots][BM][head_dim] unnormalised partial O
+  size_t ml_part = 0;         // float [kSplitSlots][BM][2] partial row max (score units), sum
   size_t total = 0;
   int64_t item_cap = 0;
 };
@@ -37,6 +50,9 @@ struct WsLayout {
 // Returns false if the sizes overflow what the layout can describe.
 bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
                int32_t hidden, WsLayout* out);
+// ws_layout plus the split-KV buffers of the bf16 chunked prefill.
+bool ws_layout_split(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q, int32_t head_dim,
+                     WsLayout* out);
 
 int router_chunks(int32_t batch);
 
@@ -55,8 +71,14 @@ struct PlanArgs {
   const int32_t* cu_k;
   int batch, n_heads_q, sink, window, bm, bn;
   int4* items;
+  int32_t item_cap;       // items the list can hold
   int32_t* counters;      // [0] n_items, [1] queue head, [2] workgroups done (both zeroed)
   int32_t* n_items_out;   // nullable
+  // split-KV (split_workers > 0): budget from the total cost and this many workgroups
+  int split_workers;
+  int32_t* piece_prefix;  // [n_items + 1]
+  int32_t* slot_base;     // [n_items]
+  int32_t* split_list;    // [kSplitSlots]
 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 
@@ -76,9 +98,22 @@ struct AttnArgs {
   float* lse;
   int batch, n_heads_q, n_heads_kv, head_dim, sink, window;
   float scale;
+  // split-KV (piece_prefix non-null; bf16 kernel only): the queue hands out pieces, counters
+  // [3] = number of pieces; piece p of item i (p - piece_prefix[i] of the item's
+  // piece_prefix[i+1] - piece_prefix[i]) runs its share of the item's tile plan and, when the
+  // item has more than one piece, writes partial results to slot slot_base[i] + piece
+  const int32_t* piece_prefix;
+  const int32_t* slot_base;
+  const int32_t* n_pieces;
+  float* o_part;
+  float* ml_part;
 };
 hipError_t launch_attn_bf16(const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, int grid, hipStream_t stream);
+// Merge of the split items' partial results (after launch_attn_bf16 with split-KV): one
+// workgroup per split item (counters[4] of them), O rounded to bf16 and the LSE written.
+hipError_t launch_split_combine(const AttnArgs& a, const int32_t* split_list,
+                                const int32_t* n_split, hipStream_t stream);
 // One decode step (ea_decode.hip): per-split partial results in the workspace, then a
 // combine.  kDecodeSplit keys per split; group sizes up to kDecodeMaxGroup.
 constexpr int kDecodeSplit = 256;

@@ -92,6 +92,79 @@ __device__ int block_exclusive_scan(int v, int* total, int* scratch /* >= kNumWa
   return excl;
 }
 
+// An empty work list (every counter zero), for inputs the list cannot describe.
+__device__ void empty_list(const PlanArgs& a) {
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < 5; ++i) a.counters[i] = 0;
+    if (a.n_items_out) *a.n_items_out = 0;
+    if (a.piece_prefix) a.piece_prefix[0] = 0;
+  }
+}
+
+// Phase 6 (split-KV): every item of cost c runs as ns = min(kSplitMaxPieces, ceil(c / T))
+// pieces; T = max(kSplitMinTiles, ceil(total cost / (2 * workers))), doubled until the split
+// items' pieces fit the kSplitSlots partial-result slots.  Writes piece_prefix (first piece of
+// every item, and the total), slot_base (first slot of a split item, else -1), split_list and
+// counters[3] (pieces), counters[4] (split items).  The list order is unchanged, so the pieces
+// of one item are consecutive and long items still come first.
+__device__ void split_phase(const PlanArgs& a, int n_items, int* scratch) {
+  __shared__ unsigned long long s_sum;
+  __shared__ int s_slots;
+  const int tid = threadIdx.x;
+  __syncthreads();  // the items written in phase 5 are visible to the whole workgroup
+  if (tid == 0) s_sum = 0;
+  __syncthreads();
+  unsigned long long part = 0;
+  for (int i = tid; i < n_items; i += kPlanThreads) part += (unsigned)a.items[i].w;
+  atomicAdd(&s_sum, part);
+  __syncthreads();
+  const long long total = (long long)s_sum;
+  long long budget = (total + 2LL * a.split_workers - 1) / (2LL * a.split_workers);
+  if (budget < kSplitMinTiles) budget = kSplitMinTiles;
+  auto pieces_of = [&](int cost) -> int {
+    const long long ns = (cost + budget - 1) / budget;
+    return (int)(ns < 1 ? 1 : (ns > kSplitMaxPieces ? kSplitMaxPieces : ns));
+  };
+  for (int round = 0; round < 40; ++round) {
+    if (tid == 0) s_slots = 0;
+    __syncthreads();
+    int slots = 0;
+    for (int i = tid; i < n_items; i += kPlanThreads) {
+      const int ns = pieces_of(a.items[i].w);
+      if (ns > 1) slots += ns;
+    }
+    atomicAdd(&s_slots, slots);
+    __syncthreads();
+    const int used = s_slots;
+    __syncthreads();
+    if (used <= kSplitSlots) break;
+    budget *= 2;
+  }
+  int carry_p = 0, carry_s = 0, carry_n = 0;
+  for (int base = 0; base < n_items; base += kPlanThreads) {
+    const int i = base + tid;
+    const int ns = i < n_items ? pieces_of(a.items[i].w) : 0;
+    const int sl = ns > 1 ? ns : 0;
+    int tp, ts, tn;
+    const int ep = block_exclusive_scan(ns, &tp, scratch);
+    const int es = block_exclusive_scan(sl, &ts, scratch);
+    const int en = block_exclusive_scan(sl > 0 ? 1 : 0, &tn, scratch);
+    if (i < n_items) {
+      a.piece_prefix[i] = carry_p + ep;
+      a.slot_base[i] = sl > 0 ? carry_s + es : -1;
+      if (sl > 0) a.split_list[carry_n + en] = i;
+    }
+    carry_p += tp;
+    carry_s += ts;
+    carry_n += tn;
+  }
+  if (tid == 0) {
+    a.piece_prefix[n_items] = carry_p;
+    a.counters[3] = carry_p;
+    a.counters[4] = carry_n;
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ uint64_t keys[kPlanMaxCells];    // sort keys, then packed sorted cells
   __shared__ int cell_off[kPlanMaxCells];      // first item of every sorted cell
@@ -131,6 +204,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   if (tid == 0) qt_prefix[B] = carry;
   __syncthreads();
+  // device lengths beyond what the host sized (more cells than the LDS holds): empty list
+  if (2 * (int64_t)carry > kPlanMaxCells) {
+    empty_list(a);
+    return;
+  }
   const int n_cells = 2 * carry;
   int n_pad = 2;
   while (n_pad < n_cells) n_pad <<= 1;
@@ -188,6 +266,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     items_total += tot;
   }
   __syncthreads();
+  // more items than the list holds (device lengths beyond what the host sized): empty list
+  if (items_total > a.item_cap) {
+    empty_list(a);
+    return;
+  }
 
   // Phase 5: expansion, heads of a cell in ascending order.
   for (int p = tid; p < n_valid; p += kPlanThreads) {
@@ -207,6 +290,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.counters[2] = 0;  // workgroups finished
     if (a.n_items_out) *a.n_items_out = items_total;
   }
+  if (a.split_workers > 0) split_phase(a, items_total, scratch);
 }
 
 }  // namespace

@@ -21,7 +21,7 @@ EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_e
            "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run",
            "ea_decode_workspace_size", "ea_hybrid_attn_decode", "ea_decode_pool_layout",
            "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool",
-           "ea_hybrid_attn_prefill_chunked")
+           "ea_hybrid_attn_prefill_chunked", "ea_prefill_chunked_workspace_size")
 
 _lib = None
 
@@ -71,6 +71,8 @@ def lib():
                                                  i32, i32, P, i32, i32, f32, P, P, i64, P, sz,
                                                  P]
     L.ea_hybrid_attn_prefill_chunked.restype = i32
+    L.ea_prefill_chunked_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.ea_prefill_chunked_workspace_size.restype = sz
     L.ea_decode_pool_layout.argtypes = [P, i32, i32, i32, i32, i32, i32, P, P, P]
     L.ea_decode_pool_layout.restype = i32
     L.ea_decode_pool_fill.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32, P, P,
@@ -293,3 +295,7 @@ def hybrid_attn_prefill_chunked(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seql
         q.shape[2], _ptr(route_bits), sink, window, float(scale), _ptr(lse_out),
         _ptr(worklist_out), _capacity(worklist_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim) -> int:
+    return int(lib().ea_prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim))

@@ -165,9 +165,22 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
  * cu_seqlens_q_host / cu_seqlens_k_host: give both (host copies, checked: monotone, within
  * the bounds, Lq <= Lk per sequence, o not overlapping q, k, v) or neither.  On the device
  * a sequence with Lk < Lq gets no work and its output rows are not written.  Other
- * arguments, the workspace and worklist_out as for ea_hybrid_attn_prefill, with max_seqlen_q
- * in place of max_seqlen for the work list bound.
+ * arguments and worklist_out as for ea_hybrid_attn_prefill, with max_seqlen_q in place of
+ * max_seqlen for the work list bound.  workspace: at least
+ * ea_prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim) bytes.
+ * bf16 runs split-KV: a work item whose key-tile cost exceeds a budget set from the total
+ * cost and the device's workgroup count runs as up to 16 pieces over consecutive parts of its
+ * tiles, on different workgroups, and a third launch merges their fp32 partial results; the
+ * work list (worklist_out) is the same as without splitting.
  */
+/*
+ * Bytes of workspace ea_hybrid_attn_prefill_chunked needs: the work list and its counters
+ * plus, for split-KV, 512 partial-result slots of 256 rows x head_dim fp32 (64 MiB at
+ * head_dim 128).  0 if the sizes overflow.
+ */
+size_t ea_prefill_chunked_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q,
+                                         int32_t head_dim);
+
 ea_status ea_hybrid_attn_prefill_chunked(
     const void* q, const void* k, const void* v, void* o, ea_dtype dt,
     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* cu_seqlens_q_host,

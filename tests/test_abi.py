@@ -297,3 +297,10 @@ def test_chunked_prefill_rejects():
     k_host = (ctypes.c_int32 * 3)(0, 5000, 5100)                       # a key sequence > max_k
     assert chunked_call(cu_q_host=q_host, cu_k_host=k_host) == ea.EA_ERR_INVALID_ARG
     assert ea.last_error()
+
+
+def test_chunked_workspace_size():
+    a = ea.prefill_chunked_workspace_size(1, 4096, 32, 128)
+    assert a >= 512 * 256 * 128 * 4 + ea.workspace_size(1, 4096, 32)
+    assert ea.prefill_chunked_workspace_size(1, 4096, 32, 64) < a
+    assert ea.prefill_chunked_workspace_size(0, 4096, 32, 128) == 0

@@ -49,7 +49,8 @@ def run_chunked(q, k, v, cu_q, cu_k, route, sink, window, worklist=True, host=Tr
     mq, mk = max(lens_q), max(lens_k)
     cap = max(1, len(lens_q) * hq * -(-mq // bm))
     wl = torch.full((cap, 4), -1, dtype=torch.int32, device=dev) if worklist else None
-    ws = H.workspace(len(lens_q), mq, hq)
+    ws = torch.empty(ea.prefill_chunked_workspace_size(len(lens_q), mq, hq, d), dtype=torch.uint8,
+                     device=dev)
     ea.hybrid_attn_prefill_chunked(H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), o, H.to_gpu(cu_q),
                                    H.to_gpu(cu_k), mq, mk, H.to_gpu(route.to(torch.uint8)), sink,
                                    window, ws, cu_seqlens_q_host=cu_q.tolist() if host else None,
@@ -131,3 +132,28 @@ def test_device_chunk_longer_than_keys_is_skipped():
                             [0, s1 - s0], hq, hkv, route[bb:bb + 1].numpy(), sink, window,
                             cu_seqlens_k=[0, int(cu_k[bb + 1] - cu_k[bb])])
         H.compare(o[s0:s1], ro, torch.bfloat16, f"valid sequence {bb}", strict=False)
+
+
+def test_device_lengths_beyond_max_seqlen_give_an_empty_work_list():
+    """Without host copies the planner cannot trust the device lengths: a sequence longer than
+    max_seqlen makes more items than the work list holds, so the list comes out empty and
+    nothing is written (no item past the list's capacity, no cell past the planner's LDS)."""
+    L, hq, hkv, d = 4096, 4, 1, 128
+    g = torch.Generator().manual_seed(1)
+    q = torch.randn(L, hq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(L, hkv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(L, hkv, d, generator=g).to(torch.bfloat16)
+    dev = H.device()
+    o = torch.full((L, hq, d), -12288.0, dtype=torch.bfloat16, device=dev)
+    route = torch.tensor([[0, 1, 1, 0]], dtype=torch.uint8, device=dev)
+    cu = torch.tensor([0, L], dtype=torch.int32, device=dev)
+    ws = H.workspace(1, 256, hq)
+    ea.hybrid_attn_prefill(H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), o, cu, 256, route, 4, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == -12288.0)
+    wsc = torch.empty(ea.prefill_chunked_workspace_size(1, 256, hq, d), dtype=torch.uint8,
+                      device=dev)
+    ea.hybrid_attn_prefill_chunked(H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), o, cu, cu, 256, 256,
+                                   route, 4, 64, wsc)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == -12288.0)
