@@ -518,12 +518,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
 // Merge of a split item's pieces: for each of its rows, M = max of the pieces' reference
 // maxima, w_p = 2^((m_p - M) * scale * log2 e), O = sum_p O_p w_p / sum_p l_p w_p (fp32, one
-// bf16 rounding), LSE = M * scale + ln sum_p l_p w_p.  One workgroup per split item; a thread
-// takes 4 head dimensions of a row.
+// bf16 rounding), LSE = M * scale + ln sum_p l_p w_p.  One workgroup per (split item, block
+// of kCombineRows rows); a thread takes 4 head dimensions of a row.
+constexpr int kCombineRows = 32;
 template <int D>
 __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, const int32_t* split_list,
                                                             const int32_t* n_split) {
-  const int k = blockIdx.x;
+  const int k = blockIdx.x, rblk = blockIdx.y;
   if (k >= min(*n_split, kSplitSlots)) return;
   const int it = split_list[k];
   const int4 item = a.items[it];
@@ -532,13 +533,14 @@ __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, const in
   const int seq0 = a.cu[b];
   const int len = a.cu[b + 1] - seq0;
   const int r0 = qt * BM, nrows = min(BM, len - r0);
+  const int rbeg = rblk * kCombineRows, rend = min(nrows, rbeg + kCombineRows);
   const int ns = a.piece_prefix[it + 1] - a.piece_prefix[it];
   const int64_t slot0 = a.slot_base[it];
   const int total_tokens = a.cu[a.batch];
   const float c_log2 = a.scale * 1.4426950408889634f;
   constexpr int C4 = D / 4, RPP = 256 / C4;
   const int c = threadIdx.x % C4;
-  for (int r = threadIdx.x / C4; r < nrows; r += RPP) {
+  for (int r = rbeg + threadIdx.x / C4; r < rend; r += RPP) {
     float M = -INFINITY;
     for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ml_part[((slot0 + p) * BM + r) * 2]);
     const float Mu = M == -INFINITY ? 0.f : M;
@@ -566,10 +568,12 @@ int attn_bf16_blocks_per_cu() { return 1; }
 
 hipError_t launch_split_combine(const AttnArgs& a, const int32_t* split_list,
                                 const int32_t* n_split, hipStream_t stream) {
+  // at most kSplitSlots / 2 split items (each has >= 2 pieces), BM / kCombineRows row blocks
+  const dim3 grid(kSplitSlots / 2, BM / kCombineRows);
   if (a.head_dim == 128)
-    split_combine_kernel<128><<<kSplitSlots, 256, 0, stream>>>(a, split_list, n_split);
+    split_combine_kernel<128><<<grid, 256, 0, stream>>>(a, split_list, n_split);
   else
-    split_combine_kernel<64><<<kSplitSlots, 256, 0, stream>>>(a, split_list, n_split);
+    split_combine_kernel<64><<<grid, 256, 0, stream>>>(a, split_list, n_split);
   return hipGetLastError();
 }
 
