@@ -64,6 +64,9 @@ def _load():
         lib.oracle_worklist.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, i64,
                                         ctypes.POINTER(i64)]
         lib.oracle_worklist.restype = i32
+        lib.oracle_attn_backward.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, P, i32,
+                                             i32, dbl, P, P, P, i32]
+        lib.oracle_attn_backward.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -101,6 +104,17 @@ def _np(x, dtype):
     except ImportError:  # pragma: no cover
         pass
     return np.ascontiguousarray(np.asarray(x, dtype=dtype))
+
+
+def _f64(x):
+    """Any tensor or array (bf16 included) as a float64 numpy array, values exact."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().cpu().to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
 
 
 def max_threads() -> int:
@@ -146,6 +160,37 @@ def attn(q, k, v, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window, scale=
     if rc != 0:
         raise ValueError(f"oracle_attn failed with code {rc}")
     return o, lse
+
+
+def attn_backward(q, k, v, dout, cu_seqlens, n_heads_q, n_heads_kv, route, sink, window,
+                  scale=None, nthreads=0, cu_seqlens_k=None):
+    """fp64 gradients of the routed attention: q/dout [Tq, Hq, D], k/v [Tk, Hkv, D] (one dtype),
+    packing as for attn.  Returns (dq [Tq, Hq, D], dk [Tk, Hkv, D], dv [Tk, Hkv, D]) float64."""
+    lib = _load()
+    qa, dt = _as_elements(q)
+    ka, dtk = _as_elements(k)
+    va, dtv = _as_elements(v)
+    oa, dto = _as_elements(dout)
+    if not (dt == dtk == dtv == dto):
+        raise TypeError("q, k, v, dout must share one dtype")
+    d = int(qa.shape[-1])
+    cu = _np(cu_seqlens, np.int32)
+    batch = int(cu.shape[0] - 1)
+    cuk = cu if cu_seqlens_k is None else _np(cu_seqlens_k, np.int32)
+    r = _np(route, np.uint8).reshape(batch, n_heads_q)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.empty((int(cu[-1]), n_heads_q, d), dtype=np.float64)
+    dk = np.empty((int(cuk[-1]), n_heads_kv, d), dtype=np.float64)
+    dv = np.empty_like(dk)
+    rc = lib.oracle_attn_backward(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, oa.ctypes.data,
+                                  dt, cu.ctypes.data, cuk.ctypes.data, batch, n_heads_q,
+                                  n_heads_kv, d, r.ctypes.data, int(sink), int(window),
+                                  float(scale), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                  int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_backward failed with code {rc}")
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seqlens, n_heads_kv, route, sink, window, scale=None,
@@ -220,3 +265,54 @@ def worklist(route, cu_seqlens, n_heads_q, sink, window, bm, bn, cu_seqlens_k=No
     if rc != 0:
         raise ValueError(f"oracle_worklist failed with code {rc}")
     return items[: n.value]
+
+
+def route_backward(key_states, cu_seqlens, w1, b1, w2, b2, o_full, o_sparse, dout, tau=1.0,
+                   noise=None):
+    """fp64 gradients of the router through its straight-through decision (Elastic Attention
+    blog post, section 2.1, "training trick": Gumbel-Softmax with a straight-through estimator
+    keeps the 0/1 routing decision differentiable).  Reading: the relaxed decision is
+    r_soft = sigmoid((z + g) / tau) with g the logistic (Gumbel-difference) noise of the draw
+    (noise [B, Hq], None = 0); the forward uses the hard decision r = (z + g > 0) and the
+    output of head h is r O_sparse + (1 - r) O_full, so dL/dr = sum_t <dO_t, O_sparse_t -
+    O_full_t> over the sequence's rows; the backward takes dr/dz = r_soft (1 - r_soft) / tau.
+    Then through the router MLP z = W2 SiLU(W1 xbar + b1) + b2 and the mean pool
+    xbar_b = mean_t key_states[t] (an empty sequence pools to 0 and gets no gradient).
+    key_states [T, C]; o_full, o_sparse, dout [T, Hq, D].
+    Returns dict with dr, dz [B, Hq], dw1 [H, C], db1 [H], dw2 [Hq, H], db2 [Hq],
+    dkey_states [T, C]."""
+    ks = _f64(key_states)
+    cu = _np(cu_seqlens, np.int32)
+    W1, B1, W2, B2 = (_f64(t) for t in (w1, b1, w2, b2))
+    of, osp, do = (_f64(t) for t in (o_full, o_sparse, dout))
+    B = int(cu.shape[0] - 1)
+    hq = W2.shape[0]
+    xbar = np.zeros((B, ks.shape[1]))
+    for b in range(B):
+        if cu[b + 1] > cu[b]:
+            xbar[b] = ks[cu[b]:cu[b + 1]].sum(axis=0) / (cu[b + 1] - cu[b])
+    u = xbar @ W1.T + B1
+    sg = 1.0 / (1.0 + np.exp(-u))
+    hs = u * sg
+    z = hs @ W2.T + B2
+    g = np.zeros_like(z) if noise is None else _f64(noise)
+    r_soft = 1.0 / (1.0 + np.exp(-(z + g) / tau))
+    dr = np.zeros((B, hq))
+    for b in range(B):
+        dr[b] = np.einsum("thd,thd->h", do[cu[b]:cu[b + 1]],
+                          osp[cu[b]:cu[b + 1]] - of[cu[b]:cu[b + 1]])
+    dz = dr * r_soft * (1.0 - r_soft) / tau
+    dw2 = dz.T @ hs
+    db2 = dz.sum(axis=0)
+    dhs = dz @ W2
+    du = dhs * (sg + u * sg * (1.0 - sg))
+    dw1 = du.T @ xbar
+    db1 = du.sum(axis=0)
+    dxbar = du @ W1
+    dks = np.zeros_like(ks)
+    for b in range(B):
+        n = cu[b + 1] - cu[b]
+        if n > 0:
+            dks[cu[b]:cu[b + 1]] = dxbar[b] / n
+    return {"dr": dr, "dz": dz, "dw1": dw1, "db1": db1, "dw2": dw2, "db2": db2,
+            "dkey_states": dks, "z": z, "r_soft": r_soft}

@@ -367,6 +367,107 @@ int oracle_worklist(const uint8_t* route, const int32_t* cu_seqlens, const int32
   return 0;
 }
 
+/*
+ * Backward of the routed attention (training of the method: [Blog §2.1] "training trick":
+ * gradients must flow through the model; here the attention part of them), straight from
+ * the chain rule of the definition above, per sequence b, query head h, row i:
+ *   P_ij = exp(x_ij - m_i) / sum_j exp(x_ij - m_i) over visible j,  o_i = sum_j P_ij v_j,
+ *   D_i = <dO_i, o_i>,  dP_ij = <dO_i, v_j>,  dS_ij = P_ij (dP_ij - D_i),
+ *   dq_i = scale * sum_j dS_ij k_j,  dk_j += scale * dS_ij q_i,  dv_j += P_ij dO_i,
+ * dk and dv summed over the query heads that read KV head g.  Same layouts and packing as
+ * oracle_attn (cu_k: optional key packing); outputs are doubles: dq [Tq, hq, d],
+ * dk / dv [Tk, hkv, d] (overwritten).  One task per (sequence, KV head), so dk and dv are
+ * accumulated by one thread.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_attn_backward(const void* q, const void* k, const void* v, const void* dout,
+                         int dtype, const int32_t* cu_seqlens, const int32_t* cu_k, int batch,
+                         int hq, int hkv, int d, const uint8_t* route, int sink, int window,
+                         double scale, double* dq_out, double* dk_out, double* dv_out,
+                         int nthreads) {
+  if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || d < 1 || window < 1 || sink < 0)
+    return -1;
+  if (cu_k == NULL) cu_k = cu_seqlens;
+  const int group = hq / hkv;
+  int64_t max_len = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)cu_seqlens[b + 1] - cu_seqlens[b];
+    const int64_t len_k = (int64_t)cu_k[b + 1] - cu_k[b];
+    if (len < 0 || len_k < len) return -1;
+    if (len_k > max_len) max_len = len_k;
+  }
+  memset(dq_out, 0, sizeof(double) * (size_t)cu_seqlens[batch] * hq * d);
+  memset(dk_out, 0, sizeof(double) * (size_t)cu_k[batch] * hkv * d);
+  memset(dv_out, 0, sizeof(double) * (size_t)cu_k[batch] * hkv * d);
+  const int64_t n_tasks = (int64_t)batch * hkv;
+  int bad = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel reduction(| : bad)
+  {
+    double* x = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!x || !o) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < n_tasks; ++task) {
+      if (!x || !o) continue;
+      const int b = (int)(task / hkv), g = (int)(task % hkv);
+      const int64_t q0 = cu_seqlens[b], nq = cu_seqlens[b + 1] - q0;
+      const int64_t k0 = cu_k[b], nk = cu_k[b + 1] - k0;
+      for (int hh = 0; hh < group; ++hh) {
+        const int h = g * group + hh;
+        const int sparse = route[(int64_t)b * hq + h] != 0;
+        for (int64_t r = 0; r < nq; ++r) {
+          const int64_t t = q0 + r;
+          const int64_t i = nk - nq + r;  /* position of the query */
+          double m = -INFINITY;
+          for (int64_t j = 0; j <= i; ++j) {
+            if (!key_visible(i, j, sparse, sink, window)) continue;
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+              dot += elem(q, dtype, (t * hq + h) * (int64_t)d + e) *
+                     elem(k, dtype, ((k0 + j) * hkv + g) * (int64_t)d + e);
+            x[j] = scale * dot;
+            if (x[j] > m) m = x[j];
+          }
+          double sum = 0.0;
+          for (int64_t j = 0; j <= i; ++j)
+            if (key_visible(i, j, sparse, sink, window)) sum += exp(x[j] - m);
+          /* P_ij stored back into x; o_i and D_i */
+          for (int e = 0; e < d; ++e) o[e] = 0.0;
+          for (int64_t j = 0; j <= i; ++j) {
+            if (!key_visible(i, j, sparse, sink, window)) continue;
+            x[j] = exp(x[j] - m) / sum;
+            for (int e = 0; e < d; ++e)
+              o[e] += x[j] * elem(v, dtype, ((k0 + j) * hkv + g) * (int64_t)d + e);
+          }
+          double Di = 0.0;
+          for (int e = 0; e < d; ++e) Di += elem(dout, dtype, (t * hq + h) * (int64_t)d + e) * o[e];
+          for (int64_t j = 0; j <= i; ++j) {
+            if (!key_visible(i, j, sparse, sink, window)) continue;
+            double dp = 0.0;
+            for (int e = 0; e < d; ++e)
+              dp += elem(dout, dtype, (t * hq + h) * (int64_t)d + e) *
+                    elem(v, dtype, ((k0 + j) * hkv + g) * (int64_t)d + e);
+            const double ds = x[j] * (dp - Di);
+            for (int e = 0; e < d; ++e) {
+              dq_out[(t * hq + h) * (int64_t)d + e] +=
+                  scale * ds * elem(k, dtype, ((k0 + j) * hkv + g) * (int64_t)d + e);
+              dk_out[((k0 + j) * hkv + g) * (int64_t)d + e] +=
+                  scale * ds * elem(q, dtype, (t * hq + h) * (int64_t)d + e);
+              dv_out[((k0 + j) * hkv + g) * (int64_t)d + e] +=
+                  x[j] * elem(dout, dtype, (t * hq + h) * (int64_t)d + e);
+            }
+          }
+        }
+      }
+    }
+    free(x);
+    free(o);
+  }
+  return bad ? -2 : 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

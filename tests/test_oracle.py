@@ -563,3 +563,109 @@ def test_chunk_flops_closed_form(lk, lq, sink, window):
     for sparse in (0, 1):
         want = int(lib_mask(lk, bool(sparse), sink, window)[lk - lq:].sum())
         assert metrics.chunk_flops([lk], [lq], [[sparse]], 1, sink, window) == 4 * want
+
+
+# ---- training side: attention backward and the router's straight-through gradient
+# (blog post section 2.1, "training trick": Gumbel-Softmax + straight-through estimator)
+
+def autograd_attention(q, k, v, dout, cu, route, sink, window, scale):
+    """torch autograd in fp64 over SDPA-free explicit attention with library-built masks."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    G = hq // hkv
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    loss = 0.0
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        L = s1 - s0
+        for h in range(hq):
+            m = lib_mask(L, bool(route[b][h]), sink, window)
+            sc = (qt[s0:s1, h] @ kt[s0:s1, h // G].T) * scale
+            p = torch.softmax(sc.masked_fill(~m, -math.inf), dim=-1)
+            o = p @ vt[s0:s1, h // G]
+            loss = loss + (o * torch.tensor(dout[s0:s1, h])).sum()
+    loss.backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_attn_backward_matches_autograd():
+    lens, hq, hkv, d, sink, window = [37, 1, 60], 4, 2, 8, 3, 10
+    cu = np.cumsum([0] + lens)
+    g = np.random.default_rng(41)
+    q = g.standard_normal((cu[-1], hq, d))
+    k = g.standard_normal((cu[-1], hkv, d))
+    v = g.standard_normal((cu[-1], hkv, d))
+    do = g.standard_normal((cu[-1], hq, d))
+    route = np.array([[0, 1, 1, 0], [1, 0, 1, 1], [1, 1, 0, 1]], np.uint8)
+    dq, dk, dv = oracle.attn_backward(q, k, v, do, cu, hq, hkv, route, sink, window)
+    rq, rk, rv = autograd_attention(q, k, v, do, cu, route, sink, window, 1 / math.sqrt(d))
+    assert np.abs(dq - rq).max() < 1e-10
+    assert np.abs(dk - rk).max() < 1e-10
+    assert np.abs(dv - rv).max() < 1e-10
+
+
+def test_attn_backward_chunked_matches_full_prefill_rows():
+    """With a KV prefix, the chunk rows' dq equal the full prefill's dq of those rows when the
+    earlier rows carry no output gradient; dk, dv then equal the full prefill's too."""
+    L, lq, hq, hkv, d = 50, 17, 2, 1, 8
+    g = np.random.default_rng(5)
+    q = g.standard_normal((L, hq, d))
+    k = g.standard_normal((L, hkv, d))
+    v = g.standard_normal((L, hkv, d))
+    do = g.standard_normal((L, hq, d))
+    do[:L - lq] = 0.0
+    route = np.array([[0, 1]], np.uint8)
+    fq, fk, fv = oracle.attn_backward(q, k, v, do, [0, L], hq, hkv, route, 4, 9)
+    cq, ck, cv = oracle.attn_backward(q[L - lq:], k, v, do[L - lq:], [0, lq], hq, hkv, route, 4, 9,
+                                      cu_seqlens_k=[0, L])
+    assert np.abs(cq - fq[L - lq:]).max() < 1e-12
+    assert np.abs(ck - fk).max() < 1e-12 and np.abs(cv - fv).max() < 1e-12
+
+
+def test_attn_backward_window_one_is_identity_path():
+    """s = 0, W = 1: o_i = v_i, so dv = dO (per KV head, summed over its heads), dq = dk = 0."""
+    T, hq, hkv, d = 12, 2, 1, 4
+    g = np.random.default_rng(2)
+    q, k, v = (g.standard_normal((T, h, d)) for h in (hq, hkv, hkv))
+    do = g.standard_normal((T, hq, d))
+    dq, dk, dv = oracle.attn_backward(q, k, v, do, [0, T], hq, hkv, [[1, 1]], 0, 1)
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    assert np.abs(dv[:, 0] - do.sum(axis=1)).max() < 1e-12
+
+
+def test_route_backward_matches_autograd_straight_through():
+    """The straight-through construction r = r_hard + r_soft - stop_gradient(r_soft) with
+    r_soft = sigmoid((z + g) / tau), output r O_sparse + (1 - r) O_full, router MLP and mean
+    pool, differentiated by torch autograd in fp64."""
+    lens, C, Hd, hq, d, tau = [5, 0, 9], 12, 6, 4, 3, 0.7
+    cu = np.cumsum([0] + lens)
+    gen = np.random.default_rng(8)
+    ks = gen.standard_normal((cu[-1], C))
+    w1, b1 = gen.standard_normal((Hd, C)) * 0.5, gen.standard_normal(Hd) * 0.1
+    w2, b2 = gen.standard_normal((hq, Hd)) * 0.5, gen.standard_normal(hq) * 0.1
+    of, osp, do = (gen.standard_normal((cu[-1], hq, d)) for _ in range(3))
+    noise = gen.logistic(size=(3, hq))
+    got = oracle.route_backward(ks, cu, w1, b1, w2, b2, of, osp, do, tau=tau, noise=noise)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    kst, w1t, b1t, w2t, b2t = T(ks), T(w1), T(b1), T(w2), T(b2)
+    xs = []
+    for b in range(3):
+        seg = kst[cu[b]:cu[b + 1]]
+        xs.append(seg.mean(dim=0) if lens[b] else torch.zeros(C, dtype=torch.float64))
+    xbar = torch.stack(xs)
+    z = F.linear(F.silu(F.linear(xbar, w1t, b1t)), w2t, b2t)
+    z.retain_grad()
+    r_soft = torch.sigmoid((z + torch.tensor(noise)) / tau)
+    r = (r_soft > 0.5).double() + r_soft - r_soft.detach()
+    loss = 0.0
+    for b in range(3):
+        s = slice(cu[b], cu[b + 1])
+        o = r[b][None, :, None] * torch.tensor(osp[s]) + (1 - r[b])[None, :, None] * torch.tensor(of[s])
+        loss = loss + (o * torch.tensor(do[s])).sum()
+    loss.backward()
+    for name, ref in (("dz", z.grad), ("dw1", w1t.grad), ("db1", b1t.grad), ("dw2", w2t.grad),
+                      ("db2", b2t.grad), ("dkey_states", kst.grad)):
+        assert np.abs(got[name] - ref.numpy()).max() < 1e-12, name
+    assert np.abs(got["dz"][1]).max() == 0  # the empty sequence: no rows, no routing gradient
