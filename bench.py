@@ -40,6 +40,7 @@ from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
 METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
 CHUNK_METRIC = "hybrid-attn chunked prefill (4K chunk over a 28K prefix) effective TFLOP/s"
+BACKWARD_METRIC = "hybrid-attn training backward (router STE + dq/dk/dv) effective TFLOP/s"
 DECODE_METRIC = "hybrid-attn decode step: cache GB/s (% HBM peak), 16 x 32K"
 DECODE_POOL_METRIC = "hybrid-attn decode step, pooled sink+ring cache: cache GB/s (% HBM peak), 16 x 32K"
 GOLDEN_BIAS = os.path.join(ROOT, "tests", "golden", "router_bias_qwen3_8b_32k.json")
@@ -395,12 +396,99 @@ def chunk_main(args):
     print(json.dumps(rec), flush=True)
 
 
+def backward_main(args):
+    """Training backward of the layer: the router's straight-through gradient
+    (ea_route_backward) and the routed attention's dq, dk, dv (ea_hybrid_attn_backward), with
+    the forward's O, LSE and both branch outputs resident."""
+    layer = Layer(args.workload)
+    w = layer.w
+    dev = torch.device("cuda:0")
+    T, hq, d = layer.q.shape
+    B = len(layer.lens)
+    layer.do_route()
+    lse = torch.empty(hq, T, dtype=torch.float32, device=dev)
+    ea.hybrid_attn_prefill(layer.q, layer.k, layer.v, layer.o, layer.cu, layer.max_len,
+                           layer.route, w.sink, w.window, layer.ws, lse_out=lse)
+    # the two branch outputs the straight-through router gradient compares
+    o_full, o_sp = torch.empty_like(layer.q), torch.empty_like(layer.q)
+    for val, out in ((0, o_full), (1, o_sp)):
+        r = torch.full_like(layer.route, val)
+        ea.hybrid_attn_prefill(layer.q, layer.k, layer.v, out, layer.cu, layer.max_len, r,
+                               w.sink, w.window, layer.ws)
+    do = inputs.dout(w, T).to(dev)
+    noise = inputs.logistic_noise(w, B).to(dev)
+    dq = torch.empty(T, hq, d, dtype=torch.float32, device=dev)
+    dk = torch.empty(T, w.n_heads_kv, d, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws_b = torch.empty(ea.attn_backward_workspace_size(B, layer.max_len, hq), dtype=torch.uint8,
+                       device=dev)
+    have_router = layer.router is not None
+    if have_router:
+        w1, b1, w2, b2 = layer.router
+        kv_dim, hid = layer.ks.shape[1], w1.shape[0]
+        rg = dict(dz=torch.empty(B, hq, device=dev), dw1=torch.empty_like(w1),
+                  db1=torch.empty_like(b1), dw2=torch.empty_like(w2), db2=torch.empty_like(b2))
+        dks = torch.empty(T, kv_dim, dtype=torch.float32, device=dev)
+        ws_r = torch.empty(ea.route_backward_workspace_size(B, kv_dim, hid, hq, d),
+                           dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def attn_bwd():
+        ea.hybrid_attn_backward(layer.q, layer.k, layer.v, layer.o, do, lse, layer.cu,
+                                layer.max_len, layer.route, w.sink, w.window, dq, dk, dv, ws_b)
+
+    def route_bwd():
+        if have_router:
+            ea.route_backward(layer.ks, layer.cu, w1, b1, w2, b2, o_full, o_sp, do, rg["dz"],
+                              rg["dw1"], rg["db1"], rg["dw2"], rg["db2"], ws_r, tau=1.0,
+                              noise=noise, dkey_states=dks)
+
+    def step():
+        route_bwd()
+        attn_bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, args.steps)
+    ms_attn = time_events(attn_bwd, args.steps)
+    ms_route = time_events(route_bwd, args.steps) if have_router else 0.0
+    r = layer.route.cpu().tolist()
+    F = metrics.backward_flops(layer.lens, r, d, w.sink, w.window)
+    f_dq, f_dkv = metrics.backward_kernel_flops(layer.lens, r, d, w.sink, w.window)
+    value = F / (ms * 1e-3) / 1e12
+    valu_peak = metrics.MI355X_FP32_VECTOR_TFLOPS
+    kern_tf = (f_dq + f_dkv) / (ms_attn * 1e-3) / 1e12
+    rec = {
+        "metric": BACKWARD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_backward", "batch": B, "seq_len": layer.max_len,
+                   "n_heads_q": hq, "n_heads_kv": w.n_heads_kv, "head_dim": d, "sink": w.sink,
+                   "window": w.window, "sparse_heads": int(layer.route.sum().item()),
+                   "routing": "router" if have_router else "bernoulli",
+                   "inputs": "bf16", "gradients": "fp32"},
+        "effective_tflop": round(F / 1e12, 4),
+        "attn_backward_ms": round(ms_attn, 4), "route_backward_ms": round(ms_route, 4),
+        "roofline": {"bound": "alu", "kernel": "bwd_dq_kernel + bwd_dkv_kernel (fp32 VALU)",
+                     "achieved": round(kern_tf, 2), "peak": valu_peak, "unit": "TFLOP/s",
+                     "frac": round(kern_tf / valu_peak, 4), "traffic": None,
+                     "launch_ms": round(ms_attn, 4),
+                     "note": "launch_ms is the whole ea_hybrid_attn_backward call (D, dq, dk/dv "
+                             "launches); achieved counts 6*D (dq) + 8*D (dk/dv) FLOPs per kept "
+                             "position and head"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--mode", choices=("prefill", "prefill_chunk", "decode", "decode_pool"),
+    ap.add_argument("--mode", choices=("prefill", "prefill_chunk", "decode", "decode_pool",
+                                       "backward"),
                     default="prefill")
     ap.add_argument("--chunk", type=int, default=4096, help="chunk length for --mode prefill_chunk")
     ap.add_argument("--workload", default=None,
@@ -427,6 +515,9 @@ def main():
     args.workload = args.workload or "qwen3_8b_32k"
     if args.mode == "prefill_chunk":
         chunk_main(args)
+        return
+    if args.mode == "backward":
+        backward_main(args)
         return
 
     layer = Layer(args.workload)

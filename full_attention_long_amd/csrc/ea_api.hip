@@ -753,4 +753,216 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
   return EA_OK;
 }
 
+
+size_t ea_attn_backward_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q) {
+  if (batch < 1 || max_seqlen_q < 0 || n_heads_q < 1) return 0;
+  const int64_t rows = (int64_t)batch * max_seqlen_q;
+  if (rows > ((int64_t)1 << 31) - 1 || rows * n_heads_q > ((int64_t)1 << 40)) return 0;
+  return align256((size_t)rows * n_heads_q * 4) + 256;
+}
+
+ea_status ea_hybrid_attn_backward(
+    const void* q, const void* k, const void* v, const void* o, const void* dout, ea_dtype dt,
+    const float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_heads_q, int32_t n_heads_kv,
+    int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window, float scale,
+    float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !dout || !lse || !cu_seqlens_q || !route || !dq || !dk || !dv ||
+      !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || batch > 65535) return fail(EA_ERR_INVALID_ARG, "need 1 <= batch <= 65535");
+  if (max_seqlen_q < 0 || max_seqlen_q > max_seqlen_k)
+    return fail(EA_ERR_INVALID_ARG, "need 0 <= max_seqlen_q <= max_seqlen_k");
+  if (n_heads_kv < 1 || n_heads_q < n_heads_kv || n_heads_q % n_heads_kv != 0 ||
+      n_heads_q > 65535)
+    return fail(EA_ERR_INVALID_ARG, "n_heads_q must be a positive multiple of n_heads_kv");
+  if (sink < 0 || window < 1) return fail(EA_ERR_INVALID_ARG, "need sink >= 0 and window >= 1");
+  if (isnan(scale) || isinf(scale)) return fail(EA_ERR_INVALID_ARG, "scale is not finite");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(EA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if (!cu_seqlens_k) {
+    cu_seqlens_k = cu_seqlens_q;
+    cu_seqlens_k_host = cu_seqlens_q_host;
+  }
+  if ((cu_seqlens_q_host == nullptr) != (cu_seqlens_k_host == nullptr))
+    return fail(EA_ERR_INVALID_ARG, "give both host copies of the packings or neither");
+  if (cu_seqlens_q_host) {
+    ea_status s = check_cu_host(cu_seqlens_q_host, batch, max_seqlen_q);
+    if (s != EA_OK) return s;
+    s = check_cu_host(cu_seqlens_k_host, batch, max_seqlen_k);
+    if (s != EA_OK) return s;
+    for (int32_t b = 0; b < batch; ++b)
+      if (cu_seqlens_k_host[b + 1] - cu_seqlens_k_host[b] <
+          cu_seqlens_q_host[b + 1] - cu_seqlens_q_host[b])
+        return fail(EA_ERR_INVALID_ARG, "a chunk is longer than its key sequence");
+    const size_t elem = dt == EA_BF16 ? 2 : 4;
+    const size_t tq = (size_t)cu_seqlens_q_host[batch], tk = (size_t)cu_seqlens_k_host[batch];
+    const size_t nq = tq * n_heads_q * head_dim, nkv = tk * n_heads_kv * head_dim;
+    const void* ins[6] = {q, k, v, o, dout, lse};
+    const size_t in_bytes[6] = {nq * elem, nkv * elem, nkv * elem, nq * elem, nq * elem,
+                                tq * n_heads_q * 4};
+    const void* outs[3] = {dq, dk, dv};
+    const size_t out_bytes[3] = {nq * 4, nkv * 4, nkv * 4};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 6; ++j)
+        if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+          return fail(EA_ERR_INVALID_ARG, "a gradient buffer overlaps an input");
+      for (int j = i + 1; j < 3; ++j)
+        if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+          return fail(EA_ERR_INVALID_ARG, "gradient buffers overlap");
+    }
+  } else if (dq == dk || dq == dv || dk == dv) {
+    return fail(EA_ERR_INVALID_ARG, "gradient buffers overlap");
+  }
+  const size_t need = ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q);
+  if (need == 0) return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < need)
+    return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_attn_backward_workspace_size()");
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.route = route;
+  a.delta = (float*)workspace;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.tq_cap = (int64_t)batch * max_seqlen_q;
+  a.batch = batch;
+  a.max_seqlen_q = max_seqlen_q;
+  a.max_seqlen_k = max_seqlen_k;
+  a.n_heads_q = n_heads_q;
+  a.n_heads_kv = n_heads_kv;
+  a.head_dim = head_dim;
+  a.sink = sink;
+  a.window = window;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)head_dim);
+  if (max_seqlen_k == 0) return EA_OK;  // nothing to do: every sequence is empty
+  const hipError_t e = launch_attn_backward(a, dt == EA_BF16, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention backward launch");
+  return EA_OK;
+}
+
+namespace {
+struct RouteBwdLayout {
+  int pool_chunks = 0, dr_chunks = 0;
+  size_t pool_partial = 0, x = 0, u = 0, hs = 0, du = 0, dx = 0, dr_partial = 0, total = 0;
+};
+bool route_bwd_layout(int32_t batch, int32_t kv_dim, int32_t hidden, int32_t n_heads_q,
+                      int32_t head_dim, RouteBwdLayout* L) {
+  if (batch < 1 || kv_dim < 1 || hidden < 1 || n_heads_q < 1 || head_dim < 1) return false;
+  if ((int64_t)batch * kv_dim > ((int64_t)1 << 31) || (int64_t)hidden * kv_dim > ((int64_t)1 << 31) ||
+      (int64_t)n_heads_q * head_dim > ((int64_t)1 << 24))
+    return false;
+  L->pool_chunks = router_chunks(batch);
+  L->dr_chunks = route_bwd_chunks(batch, n_heads_q * head_dim);
+  size_t at = 0;
+  auto take = [&](size_t floats) {
+    const size_t here = at;
+    at += align256(floats * 4);
+    return here;
+  };
+  L->pool_partial = take((size_t)batch * L->pool_chunks * kv_dim);
+  L->x = take((size_t)batch * kv_dim);
+  L->u = take((size_t)batch * hidden);
+  L->hs = take((size_t)batch * hidden);
+  L->du = take((size_t)batch * hidden);
+  L->dx = take((size_t)batch * kv_dim);
+  L->dr_partial = take((size_t)batch * L->dr_chunks * n_heads_q);
+  L->total = at;
+  return true;
+}
+}  // namespace
+
+size_t ea_route_backward_workspace_size(int32_t batch, int32_t kv_dim, int32_t hidden,
+                                        int32_t n_heads_q, int32_t head_dim) {
+  RouteBwdLayout L;
+  return route_bwd_layout(batch, kv_dim, hidden, n_heads_q, head_dim, &L) ? L.total : 0;
+}
+
+ea_status ea_route_backward(const void* key_states, ea_dtype kdt, int32_t kv_dim,
+                            const int32_t* cu_seqlens, int32_t batch, const float* w1,
+                            const float* b1, int32_t hidden, const float* w2, const float* b2,
+                            int32_t n_heads_q, const void* o_full, const void* o_sparse,
+                            const void* dout, ea_dtype odt, int32_t head_dim, const float* noise,
+                            float tau, float* dr_out, float* dz_out, float* dw1, float* db1,
+                            float* dw2, float* db2, float* dkey_states, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (!key_states || !cu_seqlens || !w1 || !b1 || !w2 || !b2 || !o_full || !o_sparse || !dout ||
+      !dz_out || !dw1 || !db1 || !dw2 || !db2 || !workspace)
+    return fail(EA_ERR_INVALID_ARG, "null pointer argument");
+  if ((kdt != EA_BF16 && kdt != EA_F32) || (odt != EA_BF16 && odt != EA_F32))
+    return fail(EA_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 1 || batch > 65535 || kv_dim < 1 || hidden < 1 || hidden > 65535 ||
+      n_heads_q < 1 || n_heads_q > 65535)
+    return fail(EA_ERR_INVALID_ARG, "batch, kv_dim, hidden and n_heads_q out of range");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!(tau > 0.f) || isinf(tau)) return fail(EA_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (dkey_states && (kv_dim % 4 != 0 || !aligned16(dkey_states)))
+    return fail(EA_ERR_UNSUPPORTED, "dkey_states needs kv_dim % 4 == 0 and 16-byte alignment");
+  if (!aligned16(key_states) || !aligned16(o_full) || !aligned16(o_sparse) || !aligned16(dout))
+    return fail(EA_ERR_INVALID_ARG, "key_states and the outputs must be 16-byte aligned");
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  RouteBwdLayout L;
+  if (!route_bwd_layout(batch, kv_dim, hidden, n_heads_q, head_dim, &L))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < L.total)
+    return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_route_backward_workspace_size()");
+  char* ws = (char*)workspace;
+  RouteBwdArgs a{};
+  a.key_states = key_states;
+  a.cu = cu_seqlens;
+  a.w1 = w1;
+  a.b1 = b1;
+  a.w2 = w2;
+  a.b2 = b2;
+  a.o_full = o_full;
+  a.o_sparse = o_sparse;
+  a.dout = dout;
+  a.noise = noise;
+  a.tau = tau;
+  a.kdt = kdt == EA_BF16 ? 0 : 1;
+  a.odt = odt == EA_BF16 ? 0 : 1;
+  a.batch = batch;
+  a.kv_dim = kv_dim;
+  a.hidden = hidden;
+  a.n_heads_q = n_heads_q;
+  a.head_dim = head_dim;
+  a.pool_chunks = L.pool_chunks;
+  a.dr_chunks = L.dr_chunks;
+  a.pool_partial = (float*)(ws + L.pool_partial);
+  a.x = (float*)(ws + L.x);
+  a.u = (float*)(ws + L.u);
+  a.hs = (float*)(ws + L.hs);
+  a.du = (float*)(ws + L.du);
+  a.dx = (float*)(ws + L.dx);
+  a.dr_partial = (float*)(ws + L.dr_partial);
+  a.dr = dr_out;
+  a.dz = dz_out;
+  a.dw1 = dw1;
+  a.db1 = db1;
+  a.dw2 = dw2;
+  a.db2 = db2;
+  a.dkey_states = dkey_states;
+  const hipError_t e = launch_route_backward(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "router backward launch");
+  return EA_OK;
+}
+
 }  // extern "C"

@@ -156,6 +156,44 @@ struct PoolWriteArgs {
   int64_t pool_rows;
   int batch, max_seqlen, n_heads_q, n_heads_kv, head_dim, sink, window;
 };
+// Backward of the router through its straight-through decision (ea_router.hip).
+struct RouteBwdArgs {
+  const void* key_states;  // [T, kv_dim], kdt
+  const int32_t* cu;       // [batch + 1]
+  const float *w1, *b1, *w2, *b2;
+  const void *o_full, *o_sparse, *dout;  // [T, n_heads_q, head_dim], odt
+  const float* noise;      // nullable [batch, n_heads_q]
+  float tau;
+  int kdt, odt, batch, kv_dim, hidden, n_heads_q, head_dim, pool_chunks, dr_chunks;
+  // workspace
+  float *pool_partial, *x, *u, *hs, *dr_partial, *du, *dx;
+  // outputs
+  float *dr, *dz, *dw1, *db1, *dw2, *db2, *dkey_states;
+};
+int route_bwd_chunks(int32_t batch, int32_t width);
+hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t stream);
+
+// Backward of the routed attention (ea_backward.hip).
+struct BwdArgs {
+  const void* q;          // [Tq, n_heads_q, head_dim]
+  const void* k;          // [Tk, n_heads_kv, head_dim]
+  const void* v;
+  const void* o;          // forward output [Tq, n_heads_q, head_dim]
+  const void* dout;       // [Tq, n_heads_q, head_dim]
+  const float* lse;       // forward log-sum-exp [n_heads_q, Tq]
+  const int32_t* cu_q;    // [batch + 1]
+  const int32_t* cu_k;    // [batch + 1] (the same as cu_q for a plain prefill)
+  const uint8_t* route;   // [batch, n_heads_q]
+  float* delta;           // workspace [n_heads_q, Tq]
+  float* dq;              // [Tq, n_heads_q, head_dim]
+  float* dk;              // [Tk, n_heads_kv, head_dim]
+  float* dv;
+  int64_t tq_cap;         // rows the delta workspace holds per head (batch * max_seqlen_q)
+  int batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv, head_dim, sink, window;
+  float scale;
+};
+hipError_t launch_attn_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+
 hipError_t launch_pool_fill(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);
 hipError_t launch_pool_append(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);
 

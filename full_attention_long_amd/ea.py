@@ -21,7 +21,9 @@ EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_e
            "ea_route", "ea_build_worklist", "ea_hybrid_attn_prefill", "ea_hybrid_attn_run",
            "ea_decode_workspace_size", "ea_hybrid_attn_decode", "ea_decode_pool_layout",
            "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool",
-           "ea_hybrid_attn_prefill_chunked", "ea_prefill_chunked_workspace_size")
+           "ea_hybrid_attn_prefill_chunked", "ea_prefill_chunked_workspace_size",
+           "ea_attn_backward_workspace_size", "ea_hybrid_attn_backward",
+           "ea_route_backward_workspace_size", "ea_route_backward")
 
 _lib = None
 
@@ -84,6 +86,16 @@ def lib():
     L.ea_hybrid_attn_decode_pool.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P,
                                              i64, P, i32, i32, f32, P, P, sz, P]
     L.ea_hybrid_attn_decode_pool.restype = i32
+    L.ea_attn_backward_workspace_size.argtypes = [i32, i32, i32]
+    L.ea_attn_backward_workspace_size.restype = sz
+    L.ea_hybrid_attn_backward.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, i32, i32, i32, i32,
+                                          i32, i32, P, i32, i32, f32, P, P, P, P, sz, P]
+    L.ea_hybrid_attn_backward.restype = i32
+    L.ea_route_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.ea_route_backward_workspace_size.restype = sz
+    L.ea_route_backward.argtypes = [P, i32, i32, P, i32, P, P, i32, P, P, i32, P, P, P, i32, i32,
+                                    P, f32, P, P, P, P, P, P, P, P, sz, P]
+    L.ea_route_backward.restype = i32
     _lib = L
     return L
 
@@ -299,3 +311,52 @@ def hybrid_attn_prefill_chunked(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seql
 
 def prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim) -> int:
     return int(lib().ea_prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim))
+
+
+def attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q) -> int:
+    return int(lib().ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q))
+
+
+def _host_cu(cu, batch):
+    if cu is None:
+        return None
+    return (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu])
+
+
+def hybrid_attn_backward(q, k, v, o, dout, lse, cu_seqlens_q, max_seqlen_q, route_bits, sink,
+                         window, dq, dk, dv, workspace, scale=0.0, cu_seqlens_k=None,
+                         max_seqlen_k=None, cu_seqlens_q_host=None, cu_seqlens_k_host=None,
+                         stream=None):
+    """ea_hybrid_attn_backward: q/o/dout [Tq, Hq, D], k/v [Tk, Hkv, D] (one dtype), lse
+    [Hq, Tq] from the forward; dq/dk/dv fp32 outputs of the shapes of q/k/v."""
+    batch = cu_seqlens_q.numel() - 1
+    if max_seqlen_k is None:
+        max_seqlen_k = max_seqlen_q
+    _check(lib().ea_hybrid_attn_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), dtype_code(q.dtype), _ptr(lse),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _host_cu(cu_seqlens_q_host, batch),
+        _host_cu(cu_seqlens_k_host, batch), batch, max_seqlen_q, max_seqlen_k, q.shape[1],
+        k.shape[1], q.shape[2], _ptr(route_bits), sink, window, float(scale), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def route_backward_workspace_size(batch, kv_dim, hidden, n_heads_q, head_dim) -> int:
+    return int(lib().ea_route_backward_workspace_size(batch, kv_dim, hidden, n_heads_q,
+                                                      head_dim))
+
+
+def route_backward(key_states, cu_seqlens, w1, b1, w2, b2, o_full, o_sparse, dout, dz, dw1,
+                   db1, dw2, db2, workspace, tau=1.0, noise=None, dr_out=None,
+                   dkey_states=None, stream=None):
+    """ea_route_backward: key_states [T, C]; o_full/o_sparse/dout [T, Hq, D] (one dtype);
+    fp32 outputs dz [B, Hq], dw1 [H, C], db1 [H], dw2 [Hq, H], db2 [Hq], optional dr_out
+    [B, Hq] and dkey_states [T, C]."""
+    batch = cu_seqlens.numel() - 1
+    _check(lib().ea_route_backward(
+        _ptr(key_states), dtype_code(key_states.dtype), key_states.shape[1], _ptr(cu_seqlens),
+        batch, _ptr(w1), _ptr(b1), w1.shape[0], _ptr(w2), _ptr(b2), w2.shape[0], _ptr(o_full),
+        _ptr(o_sparse), _ptr(dout), dtype_code(dout.dtype), dout.shape[2], _ptr(noise),
+        float(tau), _ptr(dr_out), _ptr(dz), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2),
+        _ptr(dkey_states), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))

@@ -5,7 +5,8 @@ workload shapes.  Both the HIP path and the oracle receive the exact bytes made 
 
 Seed scheme: workload k draws stream s from ``torch.Generator().manual_seed(1000*k + s)``.
 Streams: 0 Q, 1 K, 2 V, 3 key states, 4 W1, 5 W2, 6 routing bits, 7 sequence lengths,
-8 sampled query rows.  Values are ``randn`` in fp32, rounded to bf16 with
+8 sampled query rows, 9-12 decode inputs, 13 the output gradient dO, 14 the router's
+noise draw (training).  Values are ``randn`` in fp32, rounded to bf16 with
 round-to-nearest-even by ``Tensor.to(torch.bfloat16)`` where the workload is bf16.
 
 The workloads stand in for the pages' long-context evaluations (LongBench-E/V2 and RULER
@@ -21,6 +22,7 @@ import torch
 STREAM_Q, STREAM_K, STREAM_V, STREAM_KS, STREAM_W1, STREAM_W2 = 0, 1, 2, 3, 4, 5
 STREAM_ROUTE, STREAM_LENS, STREAM_ROWS = 6, 7, 8
 STREAM_DEC_Q, STREAM_DEC_K, STREAM_DEC_V, STREAM_DEC_LENS = 9, 10, 11, 12
+STREAM_DOUT, STREAM_NOISE = 13, 14
 
 
 def seed(workload: int, stream: int) -> int:
@@ -112,6 +114,19 @@ def qkv(w: Workload, total_tokens: int):
     k = normal((total_tokens, w.n_heads_kv, w.head_dim), w.index, STREAM_K, w.dtype)
     v = normal((total_tokens, w.n_heads_kv, w.head_dim), w.index, STREAM_V, w.dtype)
     return q, k, v
+
+
+def dout(w: Workload, total_tokens: int) -> torch.Tensor:
+    """Output gradient dO [T, Hq, D] on the CPU (training)."""
+    return normal((total_tokens, w.n_heads_q, w.head_dim), w.index, STREAM_DOUT, w.dtype)
+
+
+def logistic_noise(w: Workload, batch: int) -> torch.Tensor:
+    """fp32 [batch, Hq] draw of the logistic distribution, log(u) - log(1 - u) with
+    u ~ U(0, 1) clamped to [1e-6, 1 - 1e-6] (the difference of two Gumbel draws)."""
+    u = torch.rand((batch, w.n_heads_q), generator=gen(w.index, STREAM_NOISE))
+    u = u.clamp(1e-6, 1.0 - 1e-6)
+    return (torch.log(u) - torch.log1p(-u)).float()
 
 
 def bernoulli_route(w: Workload, batch: int) -> torch.Tensor:

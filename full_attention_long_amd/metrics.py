@@ -91,3 +91,31 @@ def decode_bytes(lengths, route, n_heads_kv: int, head_dim: int, sink: int, wind
 
 MI355X_BF16_DENSE_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense (no sparsity)
 MI355X_HBM_GBPS = 8000.0
+MI355X_FP32_VECTOR_TFLOPS = 157.3   # 256 CU x 2.4 GHz x 256 FLOP/clk/CU (fp32 FMA, vector ALU)
+
+
+def backward_flops(lengths, route, head_dim: int, sink: int, window: int) -> int:
+    """Effective FLOPs of the attention backward: per kept position the five products
+    S = Q K^T (recomputed), dP = dO V^T, dV = P^T dO, dQ = dS K and dK = dS^T Q at 2*D each,
+    i.e. 10*D = 2.5 x the forward's 4*D (the usual accounting for attention backward)."""
+    return effective_flops(lengths, route, head_dim, sink, window) * 5 // 2
+
+
+def backward_kernel_flops(lengths, route, head_dim: int, sink: int, window: int):
+    """Algorithmic FLOPs of the two backward kernels as built: the dq kernel computes S, dP and
+    dQ per kept position (6*D), the dk/dv kernel S, dP, dV and dK (8*D).
+    Returns (dq_flops, dkv_flops)."""
+    pairs = 0
+    for b, L in enumerate(lengths):
+        for r in route[b]:
+            pairs += visible_pairs(L, bool(int(r)), sink, window)
+    return 6 * int(head_dim) * pairs, 8 * int(head_dim) * pairs
+
+
+def route_backward_bytes(total_tokens: int, n_heads_q: int, head_dim: int, kv_dim: int,
+                         out_elem: int, key_elem: int) -> int:
+    """Algorithmic HBM bytes of the router backward: O_full, O_sparse and dO read once
+    ([T, Hq, D] each), the key states read once for the mean pool, the fp32 key-state gradient
+    written once (the router's own weights are small)."""
+    T = int(total_tokens)
+    return 3 * T * n_heads_q * head_dim * out_elem + T * kv_dim * (key_elem + 4)

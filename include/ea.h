@@ -325,6 +325,84 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
                                      float scale, float* lse_out, void* workspace,
                                      size_t ws_bytes, void* stream);
 
+/*
+ * Training: backward of the routed attention (blog post section 2.1, "training trick": the
+ * model learns through its routed attention, so gradients flow through the full heads and
+ * the sparse heads alike; masks as in ea_hybrid_attn_prefill).  With P the forward's softmax
+ * (recomputed from lse: P_ij = exp(scale <q_i, k_j> - lse_i)) and dO the gradient of O,
+ *   D_i = <dO_i, O_i>,  dS_ij = P_ij (<dO_i, v_j> - D_i)   for visible (i, j),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i,
+ * dk and dv summed over the query heads of a KV head.  The hard routing passes gradients
+ * only through the branch each head took.
+ * q, o, dout   [Tq, n_heads_q, head_dim] and k, v [Tk, n_heads_kv, head_dim], dtype dt
+ *              (EA_BF16 or EA_F32), packed as cu_seqlens_q / cu_seqlens_k [batch + 1]
+ *              (device int32; cu_seqlens_k NULL = cu_seqlens_q, a plain prefill; else chunk
+ *              row r of sequence b sits at position Lk - Lq + r, as in
+ *              ea_hybrid_attn_prefill_chunked)
+ * lse          [n_heads_q, Tq] fp32, the forward's lse_out for the same inputs
+ * cu_seqlens_q_host / cu_seqlens_k_host: nullable host copies (both or neither; with
+ *              cu_seqlens_k NULL, pass cu_seqlens_q_host alone) that enable the host checks
+ *              of the packings and of buffer overlaps
+ * dq [Tq, n_heads_q, head_dim], dk, dv [Tk, n_heads_kv, head_dim]: fp32 outputs, every
+ *              element written (a key no row can see gets 0); they must not overlap the
+ *              inputs or each other
+ * head_dim 64 or 128; sink >= 0; window >= 1; scale <= 0 selects 1/sqrt(head_dim);
+ * batch and n_heads_q at most 65535; all tensors 16-byte aligned
+ * workspace    ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q) bytes,
+ *              256-byte aligned (the D_i values)
+ * Arithmetic in fp32 over the given dtype, fixed summation order (deterministic, no atomics).
+ * Three launches: D; dq per (64-row tile, head, sequence); dk and dv per (64-key tile, KV
+ * head, sequence).  A device packing that breaks the bounds above (a sequence longer than
+ * its max_seqlen, a chunk longer than its keys) leaves that sequence's gradients unwritten;
+ * the host copies turn it into EA_ERR_INVALID_ARG.
+ */
+size_t ea_attn_backward_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q);
+
+ea_status ea_hybrid_attn_backward(
+    const void* q, const void* k, const void* v, const void* o, const void* dout, ea_dtype dt,
+    const float* lse, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host, int32_t batch,
+    int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t n_heads_q, int32_t n_heads_kv,
+    int32_t head_dim, const uint8_t* route, int32_t sink, int32_t window, float scale,
+    float* dq, float* dk, float* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Training: gradient of the Attention Router through its straight-through decision (blog
+ * post section 2.1, "training trick": Gumbel-Softmax with a straight-through estimator).
+ * The forward routes with the hard r = (z + g > 0) and head h outputs
+ * r O_sparse + (1 - r) O_full; the backward uses r_soft = sigmoid((z + g) / tau):
+ *   dr[b, h] = sum over the rows t of sequence b of <dout[t, h], O_sparse[t, h] - O_full[t, h]>
+ *   dz = dr r_soft (1 - r_soft) / tau
+ * then the router MLP of ea_route (z = W2 SiLU(W1 x + b1) + b2, x the mean of the key states)
+ * backward: dw2 = dz^T hs, db2 = sum_b dz, du = (dz W2) SiLU'(u), dw1 = du^T x,
+ * db1 = sum_b du, and dkey_states[t] = (du W1)[b] / n_b for the n_b rows t of sequence b
+ * (an empty sequence gets no rows).
+ * key_states, cu_seqlens, w1, b1, w2, b2, kv_dim, hidden, n_heads_q: as for ea_route
+ * o_full, o_sparse, dout  [T, n_heads_q, head_dim], dtype odt: the layer's output with every
+ *              head full (route all 0) and every head sparse (route all 1), and the gradient
+ *              of the routed output; head_dim 64 or 128
+ * noise        nullable [batch, n_heads_q] fp32: the logistic noise g of the draw (NULL = 0)
+ * tau          temperature, > 0
+ * dr_out       nullable [batch, n_heads_q]; dz_out [batch, n_heads_q]; dw1 [hidden, kv_dim];
+ *              db1 [hidden]; dw2 [n_heads_q, hidden]; db2 [n_heads_q]: fp32 outputs
+ * dkey_states  nullable [T, kv_dim] fp32 (needs kv_dim % 4 == 0 and 16-byte alignment)
+ * workspace    ea_route_backward_workspace_size(batch, kv_dim, hidden, n_heads_q, head_dim)
+ *              bytes, 256-byte aligned
+ * Ten short launches in fixed summation orders (deterministic); the dr reduction streams the
+ * three [T, n_heads_q, head_dim] tensors once.
+ */
+size_t ea_route_backward_workspace_size(int32_t batch, int32_t kv_dim, int32_t hidden,
+                                        int32_t n_heads_q, int32_t head_dim);
+
+ea_status ea_route_backward(const void* key_states, ea_dtype kdt, int32_t kv_dim,
+                            const int32_t* cu_seqlens, int32_t batch, const float* w1,
+                            const float* b1, int32_t hidden, const float* w2, const float* b2,
+                            int32_t n_heads_q, const void* o_full, const void* o_sparse,
+                            const void* dout, ea_dtype odt, int32_t head_dim, const float* noise,
+                            float tau, float* dr_out, float* dz_out, float* dw1, float* db1,
+                            float* dw2, float* db2, float* dkey_states, void* workspace,
+                            size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -304,3 +304,93 @@ def test_chunked_workspace_size():
     assert a >= 512 * 256 * 128 * 4 + ea.workspace_size(1, 4096, 32)
     assert ea.prefill_chunked_workspace_size(1, 4096, 32, 64) < a
     assert ea.prefill_chunked_workspace_size(0, 4096, 32, 128) == 0
+
+
+def backward_call(**kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000,
+                do=FAKE + 0x4000000, dt=ea.EA_BF16, lse=FAKE + 0x5000000, cu_q=FAKE,
+                cu_k=None, cu_q_host=None, cu_k_host=None, batch=1, max_q=1024, max_k=1024,
+                hq=32, hkv=8, d=128, route=FAKE, sink=128, window=1024, scale=0.0,
+                dq=FAKE + 0x6000000, dk=FAKE + 0x7000000, dv=FAKE + 0x8000000, ws=0x40000000,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return ea.lib().ea_hybrid_attn_backward(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ea.EA_ERR_INVALID_ARG),
+    (dict(lse=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dq=None), ea.EA_ERR_INVALID_ARG),
+    (dict(ws=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dt=7), ea.EA_ERR_INVALID_ARG),
+    (dict(batch=0), ea.EA_ERR_INVALID_ARG),
+    (dict(max_q=2048), ea.EA_ERR_INVALID_ARG),        # beyond max_seqlen_k
+    (dict(hq=12, hkv=8), ea.EA_ERR_INVALID_ARG),
+    (dict(window=0), ea.EA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ea.EA_ERR_INVALID_ARG),
+    (dict(d=96), ea.EA_ERR_UNSUPPORTED),
+    (dict(dk=FAKE + 0x7000004), ea.EA_ERR_INVALID_ARG),  # misaligned
+    (dict(ws=0x40000010), ea.EA_ERR_INVALID_ARG),         # workspace not 256-aligned
+    (dict(dv=FAKE + 0x7000000), ea.EA_ERR_INVALID_ARG),   # dv is dk
+    (dict(ws_bytes=1024), ea.EA_ERR_WORKSPACE),
+])
+def test_backward_rejects(kw, status):
+    assert backward_call(**kw) == status
+    assert ea.last_error()
+
+
+def test_backward_host_checks():
+    q_host = (ctypes.c_int32 * 2)(0, 100)
+    # a gradient overlapping an input inside its extent
+    assert backward_call(cu_q_host=q_host, dq=FAKE + 0x1000000 + 0x100) == ea.EA_ERR_INVALID_ARG
+    # only one host copy with an explicit key packing
+    assert backward_call(cu_k=FAKE + 0x100, cu_q_host=q_host) == ea.EA_ERR_INVALID_ARG
+    k_host = (ctypes.c_int32 * 2)(0, 90)                     # chunk of 100 rows over 90 keys
+    assert backward_call(cu_k=FAKE + 0x100, cu_q_host=q_host,
+                         cu_k_host=k_host) == ea.EA_ERR_INVALID_ARG
+    long_host = (ctypes.c_int32 * 2)(0, 2000)                 # longer than max_seqlen_q
+    assert backward_call(cu_q_host=long_host) == ea.EA_ERR_INVALID_ARG
+
+
+def test_backward_workspace_size():
+    a = ea.attn_backward_workspace_size(2, 4096, 32)
+    assert a >= 2 * 4096 * 32 * 4
+    assert ea.attn_backward_workspace_size(0, 4096, 32) == 0
+    assert ea.attn_backward_workspace_size(1, -1, 32) == 0
+
+
+def route_backward_call(**kw):
+    args = dict(ks=FAKE, kdt=ea.EA_BF16, kv=1024, cu=FAKE, batch=2, w1=FAKE, b1=FAKE, hid=256,
+                w2=FAKE, b2=FAKE, hq=32, of=FAKE, osp=FAKE, do=FAKE, odt=ea.EA_BF16, d=128,
+                noise=None, tau=1.0, dr=None, dz=FAKE, dw1=FAKE, db1=FAKE, dw2=FAKE, db2=FAKE,
+                dks=None, ws=0x40000000, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return ea.lib().ea_route_backward(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dz=None), ea.EA_ERR_INVALID_ARG),
+    (dict(dw1=None), ea.EA_ERR_INVALID_ARG),
+    (dict(of=None), ea.EA_ERR_INVALID_ARG),
+    (dict(odt=4), ea.EA_ERR_INVALID_ARG),
+    (dict(kv=0), ea.EA_ERR_INVALID_ARG),
+    (dict(d=80), ea.EA_ERR_UNSUPPORTED),
+    (dict(tau=0.0), ea.EA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), ea.EA_ERR_INVALID_ARG),
+    (dict(dks=FAKE, kv=1022), ea.EA_ERR_UNSUPPORTED),
+    (dict(do=FAKE + 2), ea.EA_ERR_INVALID_ARG),
+    (dict(ws=0x40000004), ea.EA_ERR_INVALID_ARG),
+    (dict(ws_bytes=64), ea.EA_ERR_WORKSPACE),
+])
+def test_route_backward_rejects(kw, status):
+    assert route_backward_call(**kw) == status
+    assert ea.last_error()
+
+
+def test_route_backward_workspace_size():
+    a = ea.route_backward_workspace_size(2, 1024, 256, 32, 128)
+    assert a >= 2 * (2 * 1024 + 3 * 256) * 4
+    assert ea.route_backward_workspace_size(0, 1024, 256, 32, 128) == 0
+    assert ea.route_backward_workspace_size(2, 1024, 256, 32, 128) < \
+        ea.route_backward_workspace_size(4, 1024, 256, 32, 128)
