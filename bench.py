@@ -420,8 +420,9 @@ def backward_main(args):
     dq = torch.empty(T, hq, d, dtype=torch.float32, device=dev)
     dk = torch.empty(T, w.n_heads_kv, d, dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    ws_b = torch.empty(ea.attn_backward_workspace_size(B, layer.max_len, hq), dtype=torch.uint8,
-                       device=dev)
+    ws_b = torch.empty(ea.attn_backward_workspace_size(ea.EA_BF16, B, layer.max_len, layer.max_len,
+                                                       hq, w.n_heads_kv, d),
+                       dtype=torch.uint8, device=dev)
     have_router = layer.router is not None
     if have_router:
         w1, b1, w2, b2 = layer.router

@@ -207,6 +207,36 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
   return EA_OK;
 }
 
+// Workspace of the attention backward: D [n_heads_q][batch * max_seqlen_q], then for bf16
+// with several query heads per KV head the per-head dk and dv partials
+// [group][batch * max_seqlen_k][n_heads_kv][head_dim] (fp32 each).
+struct BwdLayout {
+  size_t delta = 0, dk_part = 0, dv_part = 0, total = 0;
+  bool parts = false;
+};
+bool bwd_layout(ea_dtype dt, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim, BwdLayout* L) {
+  if ((dt != EA_BF16 && dt != EA_F32) || batch < 1 || max_seqlen_q < 0 ||
+      max_seqlen_k < max_seqlen_q || n_heads_q < 1 || n_heads_kv < 1 || head_dim < 1 ||
+      n_heads_q % n_heads_kv != 0)
+    return false;
+  const int64_t rows_q = (int64_t)batch * max_seqlen_q, rows_k = (int64_t)batch * max_seqlen_k;
+  if (rows_q > ((int64_t)1 << 31) - 1 || rows_k > ((int64_t)1 << 31) - 1) return false;
+  const double bytes = (double)rows_k * n_heads_q * head_dim * 8.0 + (double)rows_q * n_heads_q * 4.0;
+  if (bytes > 1.0e12) return false;  // beyond any device
+  L->delta = 0;
+  size_t at = align256((size_t)rows_q * n_heads_q * 4) + 256;
+  L->parts = dt == EA_BF16 && n_heads_q > n_heads_kv;
+  if (L->parts) {
+    const size_t part = align256((size_t)rows_k * n_heads_q * head_dim * 4);  // G slices
+    L->dk_part = at;
+    L->dv_part = at + part;
+    at += 2 * part;
+  }
+  L->total = at;
+  return true;
+}
+
 }  // namespace
 
 bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
@@ -754,11 +784,13 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
 }
 
 
-size_t ea_attn_backward_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q) {
-  if (batch < 1 || max_seqlen_q < 0 || n_heads_q < 1) return 0;
-  const int64_t rows = (int64_t)batch * max_seqlen_q;
-  if (rows > ((int64_t)1 << 31) - 1 || rows * n_heads_q > ((int64_t)1 << 40)) return 0;
-  return align256((size_t)rows * n_heads_q * 4) + 256;
+size_t ea_attn_backward_workspace_size(ea_dtype dt, int32_t batch, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t n_heads_q,
+                                       int32_t n_heads_kv, int32_t head_dim) {
+  BwdLayout L;
+  return bwd_layout(dt, batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv, head_dim, &L)
+             ? L.total
+             : 0;
 }
 
 ea_status ea_hybrid_attn_backward(
@@ -788,6 +820,9 @@ ea_status ea_hybrid_attn_backward(
     return fail(EA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (((uintptr_t)workspace & 255) != 0)
     return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  if ((int64_t)max_seqlen_k * n_heads_kv * head_dim * 4 >= ((int64_t)1 << 31) ||
+      (int64_t)max_seqlen_k * n_heads_q * head_dim * 4 >= ((int64_t)1 << 31))
+    return fail(EA_ERR_UNSUPPORTED, "sequence too long for 32-bit per-sequence addressing");
   if (!cu_seqlens_k) {
     cu_seqlens_k = cu_seqlens_q;
     cu_seqlens_k_host = cu_seqlens_q_host;
@@ -822,9 +857,10 @@ ea_status ea_hybrid_attn_backward(
   } else if (dq == dk || dq == dv || dk == dv) {
     return fail(EA_ERR_INVALID_ARG, "gradient buffers overlap");
   }
-  const size_t need = ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q);
-  if (need == 0) return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
-  if (ws_bytes < need)
+  BwdLayout WL;
+  if (!bwd_layout(dt, batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv, head_dim, &WL))
+    return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");
+  if (ws_bytes < WL.total)
     return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_attn_backward_workspace_size()");
   BwdArgs a{};
   a.q = q;
@@ -841,6 +877,9 @@ ea_status ea_hybrid_attn_backward(
   a.dk = dk;
   a.dv = dv;
   a.tq_cap = (int64_t)batch * max_seqlen_q;
+  a.tk_cap = (int64_t)batch * max_seqlen_k;
+  a.dk_part = WL.parts ? (float*)((char*)workspace + WL.dk_part) : nullptr;
+  a.dv_part = WL.parts ? (float*)((char*)workspace + WL.dv_part) : nullptr;
   a.batch = batch;
   a.max_seqlen_q = max_seqlen_q;
   a.max_seqlen_k = max_seqlen_k;

@@ -11,8 +11,9 @@
 // dK and dV summed over the query heads of a KV head.  P is recomputed from the forward's
 // log-sum-exp: P_ij = exp(scale <q_i, k_j> - lse_i).
 //
-// Design (correctness first; fp32 arithmetic on the vector ALU, deterministic, no atomics):
-//   * bwd_delta_kernel: D for every (row, head).
+// Design (fp32 inputs; bf16 inputs take the matrix-core kernels of ea_backward_bf16.hip after
+// the D kernel here; fp32 arithmetic on the vector ALU, deterministic, no atomics):
+//   * bwd_delta_kernel: D for every (row, head), both dtypes.
 //   * bwd_dq_kernel: one workgroup per (64-row q-tile, head, sequence), 4 threads per row
 //     (D/4 dimensions each); the item's key tiles (the forward's visit plan) staged through LDS
 //     as fp32; per key: two 4-lane dot products (score, dP), then dQ += dS k.
@@ -251,10 +252,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(BwdArgs a) {
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
-  if (a.max_seqlen_q > 0) {  // no query rows: no D and no dq, but dk = dv = 0 below
+  if (a.max_seqlen_q > 0) {
     bwd_delta_kernel<T><<<1024, 256, 0, stream>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  // bf16: the matrix-core kernels; fp32: the vector-ALU kernels below
+  if constexpr (sizeof(T) == 2) return launch_attn_backward_bf16_mfma(a, stream);
+  if (a.max_seqlen_q > 0) {  // no query rows: no dq, but dk = dv = 0 below
     bwd_dq_kernel<T, D><<<dim3((a.max_seqlen_q + kBwdRows - 1) / kBwdRows, a.n_heads_q,
                                a.batch),
                           kBwdThreads, 0, stream>>>(a);

@@ -189,10 +189,15 @@ struct BwdArgs {
   float* dk;              // [Tk, n_heads_kv, head_dim]
   float* dv;
   int64_t tq_cap;         // rows the delta workspace holds per head (batch * max_seqlen_q)
+  int64_t tk_cap;         // key rows a dk/dv partial holds (batch * max_seqlen_k)
+  float* dk_part;         // bf16 path with n_heads_q > n_heads_kv: per-query-head partials
+  float* dv_part;         // [group][tk_cap][n_heads_kv][head_dim], summed by a reduce kernel
   int batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv, head_dim, sink, window;
   float scale;
 };
 hipError_t launch_attn_backward(const BwdArgs& a, bool bf16, hipStream_t stream);
+// dq and dk/dv of bf16 inputs on the matrix cores (ea_backward_bf16.hip); D already computed.
+hipError_t launch_attn_backward_bf16_mfma(const BwdArgs& a, hipStream_t stream);
 
 hipError_t launch_pool_fill(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);
 hipError_t launch_pool_append(const PoolWriteArgs& a, int elem_bytes, hipStream_t stream);

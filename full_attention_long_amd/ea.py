@@ -86,7 +86,7 @@ def lib():
     L.ea_hybrid_attn_decode_pool.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P,
                                              i64, P, i32, i32, f32, P, P, sz, P]
     L.ea_hybrid_attn_decode_pool.restype = i32
-    L.ea_attn_backward_workspace_size.argtypes = [i32, i32, i32]
+    L.ea_attn_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.ea_attn_backward_workspace_size.restype = sz
     L.ea_hybrid_attn_backward.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, i32, i32, i32, i32,
                                           i32, i32, P, i32, i32, f32, P, P, P, P, sz, P]
@@ -313,8 +313,10 @@ def prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim) -> 
     return int(lib().ea_prefill_chunked_workspace_size(batch, max_seqlen_q, n_heads_q, head_dim))
 
 
-def attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q) -> int:
-    return int(lib().ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q))
+def attn_backward_workspace_size(dt, batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv,
+                                 head_dim) -> int:
+    return int(lib().ea_attn_backward_workspace_size(dt, batch, max_seqlen_q, max_seqlen_k,
+                                                     n_heads_q, n_heads_kv, head_dim))
 
 
 def _host_cu(cu, batch):

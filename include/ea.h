@@ -347,16 +347,24 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
  *              element written (a key no row can see gets 0); they must not overlap the
  *              inputs or each other
  * head_dim 64 or 128; sink >= 0; window >= 1; scale <= 0 selects 1/sqrt(head_dim);
- * batch and n_heads_q at most 65535; all tensors 16-byte aligned
- * workspace    ea_attn_backward_workspace_size(batch, max_seqlen_q, n_heads_q) bytes,
- *              256-byte aligned (the D_i values)
- * Arithmetic in fp32 over the given dtype, fixed summation order (deterministic, no atomics).
- * Three launches: D; dq per (64-row tile, head, sequence); dk and dv per (64-key tile, KV
- * head, sequence).  A device packing that breaks the bounds above (a sequence longer than
+ * batch and n_heads_q at most 65535; all tensors 16-byte aligned; one sequence's rows of
+ * q (or k) in fp32 below 2^31 bytes (max_seqlen_k * n_heads_q * head_dim * 4), else
+ * EA_ERR_UNSUPPORTED
+ * workspace    ea_attn_backward_workspace_size(dt, batch, max_seqlen_q, max_seqlen_k,
+ *              n_heads_q, n_heads_kv, head_dim) bytes, 256-byte aligned: the D_i values, and
+ *              for EA_BF16 with several query heads per KV head the per-query-head fp32
+ *              partials of dk and dv (2 * batch * max_seqlen_k * n_heads_q * head_dim * 4 bytes)
+ * EA_BF16: products on the matrix cores (bf16 operands: the inputs, and P and dS rounded to
+ * bf16; fp32 accumulation); EA_F32: fp32 arithmetic throughout.  Fixed summation orders
+ * (deterministic, no atomics).  Launches: D; dq per (q-tile, query head, sequence); dk and dv
+ * per (key tile, KV head or, for EA_BF16, query head, sequence); for EA_BF16 with several
+ * query heads per KV head a reduce adding the partials in head order.  A device packing that breaks the bounds above (a sequence longer than
  * its max_seqlen, a chunk longer than its keys) leaves that sequence's gradients unwritten;
  * the host copies turn it into EA_ERR_INVALID_ARG.
  */
-size_t ea_attn_backward_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q);
+size_t ea_attn_backward_workspace_size(ea_dtype dt, int32_t batch, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t n_heads_q,
+                                       int32_t n_heads_kv, int32_t head_dim);
 
 ea_status ea_hybrid_attn_backward(
     const void* q, const void* k, const void* v, const void* o, const void* dout, ea_dtype dt,

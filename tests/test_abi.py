@@ -353,10 +353,17 @@ def test_backward_host_checks():
 
 
 def test_backward_workspace_size():
-    a = ea.attn_backward_workspace_size(2, 4096, 32)
+    f = ea.attn_backward_workspace_size
+    a = f(ea.EA_F32, 2, 4096, 4096, 32, 8, 128)
     assert a >= 2 * 4096 * 32 * 4
-    assert ea.attn_backward_workspace_size(0, 4096, 32) == 0
-    assert ea.attn_backward_workspace_size(1, -1, 32) == 0
+    # bf16 with 4 query heads per KV head: plus per-head dk and dv partials
+    b = f(ea.EA_BF16, 2, 4096, 8192, 32, 8, 128)
+    assert b >= a + 2 * 2 * 8192 * 32 * 128 * 4
+    assert f(ea.EA_BF16, 2, 4096, 8192, 8, 8, 128) < b      # one query head per KV head
+    assert f(ea.EA_F32, 0, 4096, 4096, 32, 8, 128) == 0
+    assert f(ea.EA_F32, 1, -1, 4096, 32, 8, 128) == 0
+    assert f(ea.EA_F32, 1, 4096, 1024, 32, 8, 128) == 0     # max_seqlen_q > max_seqlen_k
+    assert f(7, 1, 16, 16, 4, 2, 64) == 0
 
 
 def route_backward_call(**kw):

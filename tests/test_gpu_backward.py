@@ -72,7 +72,8 @@ def run_backward(q, k, v, o, do, lse, cu_q, route, sink, window, cu_k=None, max_
     dq = torch.full(q.shape, fill, dtype=torch.float32, device=dev)
     dk = torch.full(k.shape, fill, dtype=torch.float32, device=dev)
     dv = torch.full(v.shape, fill, dtype=torch.float32, device=dev)
-    ws = torch.empty(ea.attn_backward_workspace_size(len(lens_q), mq, q.shape[1]),
+    ws = torch.empty(ea.attn_backward_workspace_size(ea.dtype_code(q.dtype), len(lens_q), mq, mk,
+                                                     q.shape[1], k.shape[1], q.shape[2]),
                      dtype=torch.uint8, device=dev)
     ea.hybrid_attn_backward(
         H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), H.to_gpu(o), H.to_gpu(do), H.to_gpu(lse),
