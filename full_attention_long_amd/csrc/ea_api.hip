@@ -207,11 +207,12 @@ ea_status enqueue_attn(const void* q, const void* k, const void* v, void* o, ea_
   return EA_OK;
 }
 
-// Workspace of the attention backward: D [n_heads_q][batch * max_seqlen_q], then for bf16
-// with several query heads per KV head the per-head dk and dv partials
+// Workspace of the attention backward: D [n_heads_q][batch * max_seqlen_q]; for bf16 then
+// lse * log2(e) of the same shape and, with several query heads per KV head, the per-head dk
+// and dv partials
 // [group][batch * max_seqlen_k][n_heads_kv][head_dim] (fp32 each).
 struct BwdLayout {
-  size_t delta = 0, dk_part = 0, dv_part = 0, total = 0;
+  size_t delta = 0, lse2 = 0, dk_part = 0, dv_part = 0, total = 0;
   bool parts = false;
 };
 bool bwd_layout(ea_dtype dt, int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -226,6 +227,10 @@ bool bwd_layout(ea_dtype dt, int32_t batch, int32_t max_seqlen_q, int32_t max_se
   if (bytes > 1.0e12) return false;  // beyond any device
   L->delta = 0;
   size_t at = align256((size_t)rows_q * n_heads_q * 4) + 256;
+  if (dt == EA_BF16) {  // lse in base-2 units, staged by the matrix-core kernels
+    L->lse2 = at;
+    at += align256((size_t)rows_q * n_heads_q * 4) + 256;
+  }
   L->parts = dt == EA_BF16 && n_heads_q > n_heads_kv;
   if (L->parts) {
     const size_t part = align256((size_t)rows_k * n_heads_q * head_dim * 4);  // G slices
@@ -878,6 +883,7 @@ ea_status ea_hybrid_attn_backward(
   a.dv = dv;
   a.tq_cap = (int64_t)batch * max_seqlen_q;
   a.tk_cap = (int64_t)batch * max_seqlen_k;
+  a.lse2 = dt == EA_BF16 ? (float*)((char*)workspace + WL.lse2) : nullptr;
   a.dk_part = WL.parts ? (float*)((char*)workspace + WL.dk_part) : nullptr;
   a.dv_part = WL.parts ? (float*)((char*)workspace + WL.dv_part) : nullptr;
   a.batch = batch;

@@ -13,7 +13,7 @@
 //
 // Design (fp32 inputs; bf16 inputs take the matrix-core kernels of ea_backward_bf16.hip after
 // the D kernel here; fp32 arithmetic on the vector ALU, deterministic, no atomics):
-//   * bwd_delta_kernel: D for every (row, head), both dtypes.
+//   * bwd_delta_kernel: D for every (row, head), both dtypes (and lse * log2(e) for bf16).
 //   * bwd_dq_kernel: one workgroup per (64-row q-tile, head, sequence), 4 threads per row
 //     (D/4 dimensions each); the item's key tiles (the forward's visit plan) staged through LDS
 //     as fp32; per key: two 4-lane dot products (score, dP), then dQ += dS k.
@@ -43,24 +43,46 @@ __device__ __forceinline__ bool visible(int i, int j, bool sparse, int sink, int
   return j <= i && (!sparse || j < sink || j > i - window);
 }
 
-// D[h * Tq + t] = <dO[t, h, :], O[t, h, :]>: one wavefront per (t, h) pair group
-template <typename T>
+// D[h * Tq + t] = <dO[t, h, :], O[t, h, :]> (and lse2 = lse * log2(e) for the matrix-core
+// kernels): each lane reads one 16-byte chunk of a (t, h) row, the D*elt/16 lanes of a row add
+// their partial sums in lane order (butterfly), a grid-stride loop over the rows.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
+  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int LPR = D / EPC;          // lanes per row (8..32)
+  constexpr int RPB = 256 / LPR;        // rows per workgroup pass
   const int Tq = a.cu_q[a.batch];
   if (Tq < 0 || Tq > a.tq_cap) return;  // packing beyond the host's sizing: nothing written
   const int64_t n = (int64_t)Tq * a.n_heads_q;
-  const int D = a.head_dim;
-  const int lane = threadIdx.x & 63;
-  for (int64_t w = (blockIdx.x * 4 + (threadIdx.x >> 6)); w < n; w += (int64_t)gridDim.x * 4) {
-    const int64_t t = w / a.n_heads_q;
-    const int h = (int)(w % a.n_heads_q);
-    const T* o = (const T*)a.o + (t * a.n_heads_q + h) * D;
-    const T* g = (const T*)a.dout + (t * a.n_heads_q + h) * D;
+  const int sub = threadIdx.x % LPR;
+  for (int64_t w = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; w - threadIdx.x / LPR < n;
+       w += (int64_t)gridDim.x * RPB) {
     float acc = 0.f;
-    for (int d = lane; d < D; d += 64) acc = __builtin_fmaf(ld(o, d), ld(g, d), acc);
+    if (w < n) {
+      const int64_t at = w * D + sub * EPC;  // rows [t][h] are contiguous: w = t * Hq + h
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 ro = *(const u32x4*)((const T*)a.o + at);
+        const u32x4 rg = *(const u32x4*)((const T*)a.dout + at);
+        const T* o = (const T*)&ro;
+        const T* gg = (const T*)&rg;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) a.delta[(int64_t)h * Tq + t] = acc;
+        for (int e = 0; e < EPC; ++e) acc = __builtin_fmaf((float)o[e], (float)gg[e], acc);
+      } else {
+        const f32x4 o = *(const f32x4*)((const T*)a.o + at);
+        const f32x4 gg = *(const f32x4*)((const T*)a.dout + at);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc = __builtin_fmaf(o[e], gg[e], acc);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (w < n && sub == 0) {
+      const int64_t t = w / a.n_heads_q;
+      const int h = (int)(w % a.n_heads_q);
+      a.delta[(int64_t)h * Tq + t] = acc;
+      // the matrix-core kernels stage lse in base-2 units
+      if (a.lse2) a.lse2[(int64_t)h * Tq + t] = a.lse[(int64_t)h * Tq + t] * 1.4426950408889634f;
+    }
   }
 }
 
@@ -253,7 +275,7 @@ template <typename T, int D>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipError_t e;
   if (a.max_seqlen_q > 0) {
-    bwd_delta_kernel<T><<<1024, 256, 0, stream>>>(a);
+    bwd_delta_kernel<T, D><<<2048, 256, 0, stream>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

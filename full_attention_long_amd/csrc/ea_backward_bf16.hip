@@ -36,6 +36,8 @@
 // masks are applied only on sub-tiles that hide some pair.
 #include <math.h>
 
+#include <type_traits>
+
 #include "ea_device.h"
 #include "ea_internal.h"
 
@@ -112,13 +114,32 @@ struct DkvOps {
   static constexpr int HALF = S::DT / 2;  // column-tile pairs per 16-row slice
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS of the dk/dv kernel: per buffer a Q stage and a dO stage of kRowsDkv rows (bf16,
+// swizzled as BS<D>), then lse2 and D of the stage's rows; two buffers.
+constexpr int kRowsDkv = 128;
+template <int D>
+struct DkvLds {
+  static constexpr int TILE = kRowsDkv * D * 2;
+  static constexpr int RPL = 1024 / (D * 2);         // rows one wave-wide 16-byte load fills
+  static constexpr int TILE_LOADS = TILE / 1024;     // wave-wide loads per tile
+  static constexpr int WAVE_LOADS = TILE_LOADS / kWaves;
+  static constexpr int VEC = kRowsDkv * 4;           // lse2 or D of a stage
+  static constexpr int BUF = 2 * TILE + 2 * VEC;
+  static constexpr int BYTES = 2 * BUF;
+  static constexpr int q_at(int buf) { return buf * BUF; }
+  static constexpr int g_at(int buf) { return buf * BUF + TILE; }
+  static constexpr int l_at(int buf) { return buf * BUF + 2 * TILE; }
+  static constexpr int d_at(int buf) { return buf * BUF + 2 * TILE + VEC; }
+};
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
   using S = BS<D>;
   using O = DkvOps<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * S::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][kStage];
-  __shared__ __attribute__((aligned(16))) float s_dlt[2][kStage];
+  using M = DkvLds<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[M::BYTES];
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   // longest first: every (query head, sequence) pair of key tile 0, then of tile 1, ...; the
   // pair index rotated by the tile index (XCD spread)
@@ -169,74 +190,70 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[dt][r] = dv[dt][r] = 0.f;
 
-  // rows that can see the tile: positions [max(j0, off), pe) in stages of kStage
+  // rows that can see the tile: positions [max(j0, off), pe) in stages of kRowsDkv
   const int pb0 = max(j0, off);
   const int pe = (!sparse || j0 < a.sink) ? Lk : min(Lk, j1 - 1 + a.window);
-  const int n_stages = pe > pb0 ? (pe - pb0 + kStage - 1) / kStage : 0;
+  const int n_stages = pe > pb0 ? (pe - pb0 + kRowsDkv - 1) / kRowsDkv : 0;
 
+  // Direct global -> LDS loads of a stage: the Q and dO rows [p, p + kRowsDkv) of head h
+  // (chunk rows p - off; rows past the sequence read as zero) and their lse2 and D.  Wave w
+  // issues Q and dO loads w * WAVE_LOADS .. + WAVE_LOADS - 1 (each fills RPL rows, the lane
+  // placing the logical chunk that the swizzle puts at its physical slot) and, for w < 2,
+  // the lse2 (w = 0) or D (w = 1) of 64 rows at a time.
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
-  u32x4 rq[S::LOADS], rdo[S::LOADS];
-  float rlse = 0.f, rdlt = 0.f;
-  int rpos = 0;
-  // global -> registers: Q and dO rows [p, p + kStage) of head h (positions; chunk rows
-  // p - off); lse and D raw (converted when committed, so nothing waits here)
-  const int64_t base = ((int64_t)q0 * Hq + h) * D;
+  const int64_t qbase = ((int64_t)q0 * Hq + h) * D;
   const uint32_t qbytes = (uint32_t)(Lq - 1) * q_row_bytes + D * 2;
-  const auto qr = make_rsrc((const __bf16*)a.q + base, qbytes);
-  const auto gr = make_rsrc((const __bf16*)a.dout + base, qbytes);
-  auto fetch = [&](int p) {
-    const int r0 = p - off;
+  const auto qr = make_rsrc((const __bf16*)a.q + qbase, qbytes);
+  const auto gr = make_rsrc((const __bf16*)a.dout + qbase, qbytes);
+  const auto lr = make_rsrc(a.lse2 + (int64_t)h * Tq + q0, (uint32_t)Lq * 4);
+  const auto dr = make_rsrc(a.delta + (int64_t)h * Tq + q0, (uint32_t)Lq * 4);
+  const int lrow = lane / S::CHUNKS, pc = lane % S::CHUNKS;
+  auto issue = [&](int p, int buf) {
+    const int r0 = uniform(p - off);
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / S::CHUNKS, c = idx % S::CHUNKS;
-      const uint32_t o = (uint32_t)(r0 + row) * q_row_bytes + c * 16;
-      rq[i] = buf_load16(qr, o);
-      rdo[i] = buf_load16(gr, o);
+    for (int i = 0; i < M::WAVE_LOADS; ++i) {
+      const int lg = wave * M::WAVE_LOADS + i;  // uniform
+      const int row = lg * M::RPL + lrow;
+      const uint32_t lane_off = (uint32_t)lrow * q_row_bytes + (uint32_t)((pc ^ S::swz(row)) * 16);
+      const uint32_t row_base = (uint32_t)uniform((int)((uint32_t)(r0 + lg * M::RPL) * q_row_bytes));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(lds + M::q_at(buf) + lg * 1024),
+                                               16, lane_off, row_base, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(lds + M::g_at(buf) + lg * 1024),
+                                               16, lane_off, row_base, 0, 0);
     }
-    rpos = p + (tid & (kStage - 1));
-    const int cr = min(rpos, Lk - 1) - off;  // clamped: rows past the end are masked below
-    const int64_t at = (int64_t)h * Tq + q0 + cr;
-    rlse = a.lse[at];
-    rdlt = a.delta[at];
-  };
-  auto commit = [&](int buf) {
-    unsigned char* qb = lds + (2 * buf) * S::TILE_BYTES;
-    unsigned char* gb = lds + (2 * buf + 1) * S::TILE_BYTES;
+    if (wave < 2) {
+      const auto& vr = wave == 0 ? lr : dr;
+      const int at = wave == 0 ? M::l_at(buf) : M::d_at(buf);
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / S::CHUNKS, c = idx % S::CHUNKS;
-      *(u32x4*)(qb + S::off(row, 8 * c)) = rq[i];
-      *(u32x4*)(gb + S::off(row, 8 * c)) = rdo[i];
-    }
-    if (tid < kStage) {
-      const bool ok = rpos < Lk;  // rows past the sequence: P = 0 through lse = +inf
-      s_lse[buf][tid] = ok ? rlse * kLog2e : INFINITY;
-      s_dlt[buf][tid] = ok ? rdlt : 0.f;
+      for (int i = 0; i < kRowsDkv / 64; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (lds_void*)(lds + at + i * 256), 4, (uint32_t)lane * 4,
+            (uint32_t)uniform((r0 + 64 * i) * 4), 0, 0);
     }
   };
 
-  if (n_stages > 0) {
-    fetch(pb0);
-    commit(0);
-  }
+  if (n_stages > 0) issue(pb0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int n = 0; n < n_stages; ++n) {
-    const int p_c = pb0 + n * kStage;
+    const int p_c = pb0 + n * kRowsDkv;
     const bool more = n + 1 < n_stages;
-    if (more) fetch(p_c + kStage);
+    // buffer (n + 1) & 1 was last read in stage n - 1, which every wavefront has finished
+    if (more) issue(p_c + kRowsDkv, (n + 1) & 1);
     const int buf = n & 1;
-    const unsigned char* qb = lds + (2 * buf) * S::TILE_BYTES;
-    const unsigned char* gb = lds + (2 * buf + 1) * S::TILE_BYTES;
+    const unsigned char* qb = lds + M::q_at(buf);
+    const unsigned char* gb = lds + M::g_at(buf);
+    const float* sl = (const float*)(lds + M::l_at(buf));
+    const float* sd = (const float*)(lds + M::d_at(buf));
 #pragma unroll
-    for (int j = 0; j < kStage / 32; ++j) {
+    for (int j = 0; j < kRowsDkv / 32; ++j) {
       const int i0 = p_c + 32 * j;  // first row position of the sub-tile
       // no visible pair between rows [i0, i0 + 32) and keys [kw0, kw0 + 32): skip
       const bool none = kw0 >= Lk || i0 >= Lk || i0 + 31 < kw0 ||
                         (sparse && kw0 >= a.sink && i0 - a.window + 1 > kw0 + 31);
       if (none) continue;
-      const bool full_vis = i0 >= kw0 + 31 &&
+      // every pair visible (and every row inside the sequence)
+      const bool full_vis = i0 >= kw0 + 31 && i0 + 31 < Lk &&
                             (!sparse || kw0 + 31 < a.sink || kw0 > i0 + 31 - a.window);
       f32x16 sacc, pacc;
 #pragma unroll
@@ -280,25 +297,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
         runA(c, op[c & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // P and dS: sacc[r] = S[row i0 + 8(r/4) + 4g + r%4][key]
+      // P and dS: sacc[r] = S[row i0 + 8(r/4) + 4g + r%4][key]; `masked` selects the code
+      // path once per sub-tile (uniform), the masked one hiding invisible pairs and rows past
+      // the sequence
+      auto phase_b = [&](auto masked_t) {
+        constexpr bool masked = decltype(masked_t)::value;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int lr = 32 * j + 8 * q4 + 4 * g;  // local row of r = 4 q4
-        const f32x4 l4 = *(const f32x4*)&s_lse[buf][lr];
-        const f32x4 d4 = *(const f32x4*)&s_dlt[buf][lr];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int lr4 = 32 * j + 8 * q4 + 4 * g;  // local row of r = 4 q4
+          const f32x4 l4 = *(const f32x4*)&sl[lr4];
+          const f32x4 d4 = *(const f32x4*)&sd[lr4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -l4[e]));
-          if (!full_vis) {  // uniform: the select below runs only on sub-tiles that need it
-            const int row = p_c + lr + e;
-            const bool vis = (key <= row) & (!sparse | (key < a.sink) | (key > row - a.window));
-            p = vis ? p : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -l4[e]));
+            if constexpr (masked) {
+              const int row = p_c + lr4 + e;
+              const bool vis = (row < Lk) & (key <= row) &
+                               (!sparse | (key < a.sink) | (key > row - a.window));
+              p = vis ? p : 0.f;
+            }
+            pb[r / 8][r % 8] = (__bf16)p;
+            db[r / 8][r % 8] = (__bf16)(p * (pacc[r] - d4[e]));
           }
-          pb[r / 8][r % 8] = (__bf16)p;
-          db[r / 8][r % 8] = (__bf16)(p * (pacc[r] - d4[e]));
         }
-      }
+      };
+      if (full_vis)
+        phase_b(std::false_type{});
+      else
+        phase_b(std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
       constexpr int c_first = O::NA & 1;  // buffer holding the first C group's operands
 #pragma unroll
@@ -308,7 +335,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) commit(buf ^ 1);
+    // the next stage's loads (this wavefront's share) have landed; after the barrier every
+    // wavefront's have, and nobody reads this stage's buffer any more
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -342,6 +371,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
   using S = BS<D>;
   constexpr int NA = S::KSTEPS / 2;  // S^T / dP^T groups of two k-steps
+  constexpr int RPL = 1024 / (D * 2);  // rows one wave-wide 16-byte direct load fills
+  constexpr int WAVE_LOADS = S::TILE_BYTES / 1024 / kWaves;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * S::TILE_BYTES];
   const int Hq = a.n_heads_q, Hkv = a.n_heads_kv, G = Hq / Hkv;
   // longest first: the last q-tiles (most keys) of every (head, sequence) pair first
@@ -360,9 +391,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
   if (qt * kRowTile >= Lq) return;
   const int off = Lk - Lq;
   const int tid = threadIdx.x, lane = tid & 63;
-  // the wavefront index is uniform; readfirstlane lets the compiler know, so every test
-  // built on it (skip, mask) is a scalar branch rather than a per-lane exec mask
-  const int wave = uniform(tid >> 6);
+  const int wave = uniform(tid >> 6);  // uniform: skips and masks are scalar branches
   const int l32 = lane & 31, g = lane >> 5;
   const int tr_row = 4 * g + (lane & 15) / 4;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
   }
   const bool row_ok = cr < Lq;
   const int64_t at = (int64_t)h * Tq + q0 + min(cr, Lq - 1);
-  const float lse2 = row_ok ? a.lse[at] * kLog2e : INFINITY;
+  const float lse2 = row_ok ? a.lse2[at] : INFINITY;  // rows past the sequence: P = 0
   const float dlt = row_ok ? a.delta[at] : 0.f;
   f32x16 dq[S::DT];
 #pragma unroll
@@ -410,42 +439,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
   const int count = n1 + max(0, t_hi - s2 + 1);
   auto tile_of = [&](int n) { return n < n1 ? n : s2 + (n - n1); };
 
+  // direct global -> LDS loads of a K and a V tile (keys past the sequence read as zero;
+  // lane placement as in the dk/dv kernel)
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
   const int64_t kv_base = ((int64_t)k0 * Hkv + kvh) * D;
   const uint32_t kv_bytes = (uint32_t)(Lk - 1) * kv_row_bytes + D * 2;
   const auto kr = make_rsrc((const __bf16*)a.k + kv_base, kv_bytes);
   const auto vr = make_rsrc((const __bf16*)a.v + kv_base, kv_bytes);
-  u32x4 rk[S::LOADS], rv[S::LOADS];
-  auto fetch = [&](int t) {
+  const int lrow = lane / S::CHUNKS, pc = lane % S::CHUNKS;
+  auto issue = [&](int t, int buf) {
+    const int key0 = uniform(t * kStage);
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / S::CHUNKS, c = idx % S::CHUNKS;
-      const uint32_t o = (uint32_t)(t * kStage + row) * kv_row_bytes + c * 16;
-      rk[i] = buf_load16(kr, o);
-      rv[i] = buf_load16(vr, o);
-    }
-  };
-  auto commit = [&](int buf) {
-    unsigned char* kb = lds + (2 * buf) * S::TILE_BYTES;
-    unsigned char* vb = lds + (2 * buf + 1) * S::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx / S::CHUNKS, c = idx % S::CHUNKS;
-      *(u32x4*)(kb + S::off(row, 8 * c)) = rk[i];
-      *(u32x4*)(vb + S::off(row, 8 * c)) = rv[i];
+    for (int i = 0; i < WAVE_LOADS; ++i) {
+      const int lg = wave * WAVE_LOADS + i;
+      const int row = lg * RPL + lrow;
+      const uint32_t lane_off =
+          (uint32_t)lrow * kv_row_bytes + (uint32_t)((pc ^ S::swz(row)) * 16);
+      const uint32_t row_base =
+          (uint32_t)uniform((int)((uint32_t)(key0 + lg * RPL) * kv_row_bytes));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          kr, (lds_void*)(lds + (2 * buf) * S::TILE_BYTES + lg * 1024), 16, lane_off, row_base,
+          0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vr, (lds_void*)(lds + (2 * buf + 1) * S::TILE_BYTES + lg * 1024), 16, lane_off,
+          row_base, 0, 0);
     }
   };
 
-  if (count > 0) {
-    fetch(tile_of(0));
-    commit(0);
-  }
+  if (count > 0) issue(tile_of(0), 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int n = 0; n < count; ++n) {
     const bool more = n + 1 < count;
-    if (more) fetch(tile_of(n + 1));
+    if (more) issue(tile_of(n + 1), (n + 1) & 1);
     const int buf = n & 1;
     const unsigned char* kb = lds + (2 * buf) * S::TILE_BYTES;
     const unsigned char* vb = lds + (2 * buf + 1) * S::TILE_BYTES;
@@ -498,17 +524,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
         runA(c, op[c & 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // sacc[r] = S^T[key c0 + 8(r/4) + 4g + r%4][row pos]
+      // dS: sacc[r] = S^T[key c0 + 8(r/4) + 4g + r%4][row pos]; the masked path is chosen
+      // once per sub-tile (uniform)
+      auto phase_b = [&](auto masked_t) {
+        constexpr bool masked = decltype(masked_t)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -lse2));
-        if (!full_vis) {  // uniform branch; the select runs only where some pair is hidden
-          const int kk = c0 + 8 * (r / 4) + 4 * g + r % 4;
-          const bool vis = (kk <= pos) & (!sparse | (kk < a.sink) | (kk > pos - a.window));
-          p = vis ? p : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c_log2, -lse2));
+          if constexpr (masked) {
+            const int kk = c0 + 8 * (r / 4) + 4 * g + r % 4;
+            const bool vis = (kk <= pos) & (!sparse | (kk < a.sink) | (kk > pos - a.window));
+            p = vis ? p : 0.f;
+          }
+          db[r / 8][r % 8] = (__bf16)(p * (pacc[r] - dlt));
         }
-        db[r / 8][r % 8] = (__bf16)(p * (pacc[r] - dlt));
-      }
+      };
+      if (full_vis)
+        phase_b(std::false_type{});
+      else
+        phase_b(std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
       constexpr int NC = S::DT;  // two MFMAs per group
       constexpr int c_first = NA & 1;
@@ -519,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) commit(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

@@ -185,6 +185,7 @@ struct BwdArgs {
   const int32_t* cu_k;    // [batch + 1] (the same as cu_q for a plain prefill)
   const uint8_t* route;   // [batch, n_heads_q]
   float* delta;           // workspace [n_heads_q, Tq]
+  float* lse2;            // workspace [n_heads_q, Tq]: lse * log2(e) (bf16 path; else null)
   float* dq;              // [Tq, n_heads_q, head_dim]
   float* dk;              // [Tk, n_heads_kv, head_dim]
   float* dv;

@@ -351,9 +351,10 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
  * q (or k) in fp32 below 2^31 bytes (max_seqlen_k * n_heads_q * head_dim * 4), else
  * EA_ERR_UNSUPPORTED
  * workspace    ea_attn_backward_workspace_size(dt, batch, max_seqlen_q, max_seqlen_k,
- *              n_heads_q, n_heads_kv, head_dim) bytes, 256-byte aligned: the D_i values, and
- *              for EA_BF16 with several query heads per KV head the per-query-head fp32
- *              partials of dk and dv (2 * batch * max_seqlen_k * n_heads_q * head_dim * 4 bytes)
+ *              n_heads_q, n_heads_kv, head_dim) bytes, 256-byte aligned: the D_i values; for
+ *              EA_BF16 also lse in base-2 units and, with several query heads per KV head, the
+ *              per-query-head fp32 partials of dk and dv (2 * batch * max_seqlen_k * n_heads_q
+ *              * head_dim * 4 bytes)
  * EA_BF16: products on the matrix cores (bf16 operands: the inputs, and P and dS rounded to
  * bf16; fp32 accumulation); EA_F32: fp32 arithmetic throughout.  Fixed summation orders
  * (deterministic, no atomics).  Launches: D; dq per (q-tile, query head, sequence); dk and dv
