@@ -116,26 +116,35 @@ struct DkvOps {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS of the dk/dv kernel: per buffer a Q stage and a dO stage of kRowsDkv rows (bf16,
-// swizzled as BS<D>), then lse2 and D of the stage's rows; two buffers.
-constexpr int kRowsDkv = 128;
+// LDS of the dk/dv kernel: the K and V tiles of the workgroup's kKeyTile keys, then two
+// buffers of a Q stage and a dO stage of kRowsDkv rows (bf16, swizzled as BS<D>) with their
+// lse2 and D.  After the last stage the whole area holds the partial dK, dV exchange.
+constexpr int kRowsDkv = 64;
+constexpr int kWavesDkv = 8;                 // 4 key blocks x 2 row parities
+constexpr int kThreadsDkv = 64 * kWavesDkv;
 template <int D>
 struct DkvLds {
+  static constexpr int KV_TILE = kKeyTile * D * 2;
   static constexpr int TILE = kRowsDkv * D * 2;
-  static constexpr int RPL = 1024 / (D * 2);         // rows one wave-wide 16-byte load fills
-  static constexpr int TILE_LOADS = TILE / 1024;     // wave-wide loads per tile
-  static constexpr int WAVE_LOADS = TILE_LOADS / kWaves;
-  static constexpr int VEC = kRowsDkv * 4;           // lse2 or D of a stage
+  static constexpr int RPL = 1024 / (D * 2);            // rows one wave-wide 16-byte load fills
+  static constexpr int KV_WAVE_LOADS = KV_TILE / 1024 / kWavesDkv;
+  static constexpr int WAVE_LOADS = TILE / 1024 / kWavesDkv;
+  static constexpr int VEC = kRowsDkv * 4;              // lse2 or D of a stage
   static constexpr int BUF = 2 * TILE + 2 * VEC;
-  static constexpr int BYTES = 2 * BUF;
-  static constexpr int q_at(int buf) { return buf * BUF; }
-  static constexpr int g_at(int buf) { return buf * BUF + TILE; }
-  static constexpr int l_at(int buf) { return buf * BUF + 2 * TILE; }
-  static constexpr int d_at(int buf) { return buf * BUF + 2 * TILE + VEC; }
+  static constexpr int BYTES = 2 * KV_TILE + 2 * BUF;
+  static constexpr int k_at() { return 0; }
+  static constexpr int v_at() { return KV_TILE; }
+  static constexpr int q_at(int buf) { return 2 * KV_TILE + buf * BUF; }
+  static constexpr int g_at(int buf) { return 2 * KV_TILE + buf * BUF + TILE; }
+  static constexpr int l_at(int buf) { return 2 * KV_TILE + buf * BUF + 2 * TILE; }
+  static constexpr int d_at(int buf) { return 2 * KV_TILE + buf * BUF + 2 * TILE + VEC; }
+  // partial exchange: 4 key blocks x (dK, dV) x DT x 16 registers x 64 lanes x 4 bytes
+  static constexpr int XCHG = 4 * 2 * (D / 32) * 16 * 64 * 4;
+  static_assert(XCHG <= BYTES, "the exchange reuses the tile area");
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
+__global__ __launch_bounds__(kThreadsDkv, 1) void bwd_dkv_mfma(BwdArgs a) {
   using S = BS<D>;
   using O = DkvOps<D>;
   using M = DkvLds<D>;
@@ -160,28 +169,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
   // the wavefront index is uniform; readfirstlane lets the compiler know, so every test
   // built on it (skip, mask) is a scalar branch rather than a per-lane exec mask
   const int wave = uniform(tid >> 6);
+  const int kb = wave & 3;   // key block: keys kw0 .. kw0 + 31
+  const int rp = wave >> 2;  // row parity: the sub-tile rp of every 64-row stage
   const int l32 = lane & 31, g = lane >> 5;
   const int tr_row = 4 * g + (lane & 15) / 4;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int j0 = kt * kKeyTile, j1 = min(j0 + kKeyTile, Lk);
-  const int kw0 = j0 + 32 * wave;  // this wavefront's first key
+  const int kw0 = j0 + 32 * kb;
   const int key = kw0 + l32;
   const float c_log2 = a.scale * kLog2e;
   const bool sparse = a.route[(int64_t)b * Hq + h] != 0;
+  const int lrow = lane / S::CHUNKS, pc = lane % S::CHUNKS;
 
-  // K, V of the wavefront's keys as B operands: lane holds key kw0 + l32, dims 16ks + 8g..
-  bf16x8 kreg[S::KSTEPS], vreg[S::KSTEPS];
+  // K and V tiles of the workgroup's keys, direct to LDS (keys past the sequence read as zero)
   {
     const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
     const uint32_t bytes = (uint32_t)(Lk - 1) * row_bytes + D * 2;
     const int64_t base = ((int64_t)k0 * Hkv + kvh) * D;
     const auto kr = make_rsrc((const __bf16*)a.k + base, bytes);
     const auto vr = make_rsrc((const __bf16*)a.v + base, bytes);
-    const uint32_t ro = (uint32_t)key * row_bytes;
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks) {
-      kreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(kr, ro + (16 * ks + 8 * g) * 2));
-      vreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(vr, ro + (16 * ks + 8 * g) * 2));
+    for (int i = 0; i < M::KV_WAVE_LOADS; ++i) {
+      const int lg = wave * M::KV_WAVE_LOADS + i;
+      const int row = lg * M::RPL + lrow;
+      const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)((pc ^ S::swz(row)) * 16);
+      const uint32_t row_base = (uint32_t)uniform((int)((uint32_t)(j0 + lg * M::RPL) * row_bytes));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(lds + M::k_at() + lg * 1024), 16,
+                                               lane_off, row_base, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(lds + M::v_at() + lg * 1024), 16,
+                                               lane_off, row_base, 0, 0);
     }
   }
   f32x16 dk[S::DT], dv[S::DT];
@@ -195,11 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
   const int pe = (!sparse || j0 < a.sink) ? Lk : min(Lk, j1 - 1 + a.window);
   const int n_stages = pe > pb0 ? (pe - pb0 + kRowsDkv - 1) / kRowsDkv : 0;
 
-  // Direct global -> LDS loads of a stage: the Q and dO rows [p, p + kRowsDkv) of head h
-  // (chunk rows p - off; rows past the sequence read as zero) and their lse2 and D.  Wave w
-  // issues Q and dO loads w * WAVE_LOADS .. + WAVE_LOADS - 1 (each fills RPL rows, the lane
-  // placing the logical chunk that the swizzle puts at its physical slot) and, for w < 2,
-  // the lse2 (w = 0) or D (w = 1) of 64 rows at a time.
+  // Direct loads of a stage: the Q and dO rows [p, p + kRowsDkv) of head h (chunk rows
+  // p - off; rows past the sequence read as zero) and their lse2 (wave 0) and D (wave 1).
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
   const int64_t qbase = ((int64_t)q0 * Hq + h) * D;
   const uint32_t qbytes = (uint32_t)(Lq - 1) * q_row_bytes + D * 2;
@@ -207,12 +220,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
   const auto gr = make_rsrc((const __bf16*)a.dout + qbase, qbytes);
   const auto lr = make_rsrc(a.lse2 + (int64_t)h * Tq + q0, (uint32_t)Lq * 4);
   const auto dr = make_rsrc(a.delta + (int64_t)h * Tq + q0, (uint32_t)Lq * 4);
-  const int lrow = lane / S::CHUNKS, pc = lane % S::CHUNKS;
   auto issue = [&](int p, int buf) {
     const int r0 = uniform(p - off);
 #pragma unroll
     for (int i = 0; i < M::WAVE_LOADS; ++i) {
-      const int lg = wave * M::WAVE_LOADS + i;  // uniform
+      const int lg = wave * M::WAVE_LOADS + i;
       const int row = lg * M::RPL + lrow;
       const uint32_t lane_off = (uint32_t)lrow * q_row_bytes + (uint32_t)((pc ^ S::swz(row)) * 16);
       const uint32_t row_base = (uint32_t)uniform((int)((uint32_t)(r0 + lg * M::RPL) * q_row_bytes));
@@ -221,20 +233,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(gr, (lds_void*)(lds + M::g_at(buf) + lg * 1024),
                                                16, lane_off, row_base, 0, 0);
     }
-    if (wave < 2) {
-      const auto& vr = wave == 0 ? lr : dr;
-      const int at = wave == 0 ? M::l_at(buf) : M::d_at(buf);
-#pragma unroll
-      for (int i = 0; i < kRowsDkv / 64; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vr, (lds_void*)(lds + at + i * 256), 4, (uint32_t)lane * 4,
-            (uint32_t)uniform((r0 + 64 * i) * 4), 0, 0);
-    }
+    if (wave < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wave == 0 ? lr : dr,
+          (lds_void*)(lds + (wave == 0 ? M::l_at(buf) : M::d_at(buf))), 4, (uint32_t)lane * 4,
+          (uint32_t)uniform(r0 * 4), 0, 0);
   };
 
   if (n_stages > 0) issue(pb0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const unsigned char* kvk = lds + M::k_at();
+  const unsigned char* kvv = lds + M::v_at();
   for (int n = 0; n < n_stages; ++n) {
     const int p_c = pb0 + n * kRowsDkv;
     const bool more = n + 1 < n_stages;
@@ -245,30 +255,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
     const unsigned char* gb = lds + M::g_at(buf);
     const float* sl = (const float*)(lds + M::l_at(buf));
     const float* sd = (const float*)(lds + M::d_at(buf));
-#pragma unroll
-    for (int j = 0; j < kRowsDkv / 32; ++j) {
-      const int i0 = p_c + 32 * j;  // first row position of the sub-tile
-      // no visible pair between rows [i0, i0 + 32) and keys [kw0, kw0 + 32): skip
-      const bool none = kw0 >= Lk || i0 >= Lk || i0 + 31 < kw0 ||
-                        (sparse && kw0 >= a.sink && i0 - a.window + 1 > kw0 + 31);
-      if (none) continue;
+    const int j = rp;               // this wavefront's sub-tile of the stage
+    const int i0 = p_c + 32 * j;    // its first row position
+    // no visible pair between rows [i0, i0 + 32) and keys [kw0, kw0 + 32): skip
+    const bool none = kw0 >= Lk || i0 >= Lk || i0 + 31 < kw0 ||
+                      (sparse && kw0 >= a.sink && i0 - a.window + 1 > kw0 + 31);
+    if (!none) {
       // every pair visible (and every row inside the sequence)
       const bool full_vis = i0 >= kw0 + 31 && i0 + 31 < Lk &&
                             (!sparse || kw0 + 31 < a.sink || kw0 > i0 + 31 - a.window);
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-      auto readA = [&](int c, bf16x8 (&op)[4]) {
-        op[0] = read_plain<D>(qb, 32 * j, 2 * c, l32, g);
-        op[1] = read_plain<D>(qb, 32 * j, 2 * c + 1, l32, g);
-        op[2] = read_plain<D>(gb, 32 * j, 2 * c, l32, g);
-        op[3] = read_plain<D>(gb, 32 * j, 2 * c + 1, l32, g);
+      // A: one k-step per group (S and dP), the four operands read one group ahead
+      auto readA = [&](int ks, bf16x8 (&op)[4]) {
+        op[0] = read_plain<D>(qb, 32 * j, ks, l32, g);
+        op[1] = read_plain<D>(gb, 32 * j, ks, l32, g);
+        op[2] = read_plain<D>(kvk, 32 * kb, ks, l32, g);  // K^T: lane holds key l32's dims
+        op[3] = read_plain<D>(kvv, 32 * kb, ks, l32, g);
       };
-      auto runA = [&](int c, const bf16x8 (&op)[4]) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], kreg[2 * c], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[2], vreg[2 * c], pacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[1], kreg[2 * c + 1], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[3], vreg[2 * c + 1], pacc, 0, 0, 0);
+      auto runA = [&](const bf16x8 (&op)[4]) {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], op[2], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[1], op[3], pacc, 0, 0, 0);
       };
       auto readC = [&](int c, bf16x8 (&op)[4]) {
         const int kh = c / O::HALF, dt0 = 2 * (c % O::HALF);
@@ -285,17 +293,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
         dv[dt0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[2], pb[kh], dv[dt0 + 1], 0, 0, 0);
         dk[dt0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[3], db[kh], dk[dt0 + 1], 0, 0, 0);
       };
-      bf16x8 op[2][4];
-      readA(0, op[0]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < O::NA; ++c) {
-        if (c + 1 < O::NA)
-          readA(c + 1, op[(c + 1) & 1]);
-        else
-          readC(0, op[(c + 1) & 1]);  // the first C group's operands load during the VALU
-        runA(c, op[c & 1]);
+      {
+        bf16x8 op[2][4];
+        readA(0, op[0]);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+          if (ks + 1 < S::KSTEPS) readA(ks + 1, op[(ks + 1) & 1]);
+          runA(op[ks & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // P and dS: sacc[r] = S[row i0 + 8(r/4) + 4g + r%4][key]; `masked` selects the code
       // path once per sub-tile (uniform), the masked one hiding invisible pairs and rows past
@@ -327,11 +334,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
       else
         phase_b(std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int c_first = O::NA & 1;  // buffer holding the first C group's operands
+      // C: single-buffered operands (the partner wavefront on the SIMD covers the latency)
 #pragma unroll
       for (int c = 0; c < O::NC; ++c) {
-        if (c + 1 < O::NC) readC(c + 1, op[(c + 1 + c_first) & 1]);
-        runC(c, op[(c + c_first) & 1]);
+        bf16x8 op[4];
+        readC(c, op);
+        runC(c, op);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -341,9 +349,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
     __syncthreads();
   }
 
+  // The two row parities of a key block add their partial sums through LDS (parity 1 writes,
+  // parity 0 adds, in that fixed order): lane-major float4 slots per register quad.
+  __syncthreads();  // (no stage ran: the K/V loads may still be landing in the area)
+  float* xb = (float*)lds + kb * (2 * S::DT * 16 * 64);
+  if (rp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = dk[dt][4 * q4 + e];
+          v4[e] = dv[dt][4 * q4 + e];
+        }
+        *(f32x4*)(xb + ((0 * S::DT + dt) * 4 + q4) * 256 + lane * 4) = k4;
+        *(f32x4*)(xb + ((1 * S::DT + dt) * 4 + q4) * 256 + lane * 4) = v4;
+      }
+  }
+  __syncthreads();
   // dk[dt][r] = dK^T[dim 32dt + 8(r/4) + 4g + r%4][key]; one query head's share: the
   // gradient itself when the KV head has one query head, else its partial
-  if (key < Lk) {
+  if (rp == 0 && key < Lk) {
     const int64_t at = ((int64_t)(k0 + key) * Hkv + kvh) * D;
     const int64_t slice = G > 1 ? (int64_t)hh * a.tk_cap * Hkv * D : 0;
     float* dkp = (G > 1 ? a.dk_part + slice : a.dk) + at;
@@ -353,11 +381,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(BwdArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dt + 8 * q4 + 4 * g;
+        const f32x4 k1 = *(const f32x4*)(xb + ((0 * S::DT + dt) * 4 + q4) * 256 + lane * 4);
+        const f32x4 v1 = *(const f32x4*)(xb + ((1 * S::DT + dt) * 4 + q4) * 256 + lane * 4);
         f32x4 kv4, vv4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv4[e] = dk[dt][4 * q4 + e] * a.scale;
-          vv4[e] = dv[dt][4 * q4 + e];
+          kv4[e] = (dk[dt][4 * q4 + e] + k1[e]) * a.scale;
+          vv4[e] = dv[dt][4 * q4 + e] + v1[e];
         }
         *(f32x4*)(dkp + d) = kv4;
         *(f32x4*)(dvp + d) = vv4;
@@ -601,7 +631,7 @@ hipError_t launch_mfma(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int ktiles = (a.max_seqlen_k + kKeyTile - 1) / kKeyTile;
-  bwd_dkv_mfma<D><<<ktiles * a.n_heads_q * a.batch, kThreads, 0, stream>>>(a);
+  bwd_dkv_mfma<D><<<ktiles * a.n_heads_q * a.batch, kThreadsDkv, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_heads_q == a.n_heads_kv) return e;
   bwd_dkv_reduce<<<2048, 256, 0, stream>>>(a);
