@@ -48,6 +48,8 @@ ATTN_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attn_bf1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_qwen3_8b_32k_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_decode.hip")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_qwen3_8b_32k_traffic.json")
+BWD_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_backward_bf16.hip")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_backward_qwen3_8b_32k_traffic.json")
 
 
 def source_sha256(path):
@@ -396,6 +398,37 @@ def chunk_main(args):
     print(json.dumps(rec), flush=True)
 
 
+def backward_cpu_baseline(layer: Layer, do_cpu, seconds: float):
+    """fp64 oracle backward on a bounded sample of the same layer: the last m rows of the
+    first sequence as a chunk over its whole prefix (their dq and their share of dk, dv),
+    m doubling until the time budget is spent."""
+    import numpy as np
+    import oracle
+    w = layer.w
+    q, k, v = layer.cpu
+    L = layer.lens[0]
+    route = layer.route.cpu().numpy()[:1]
+    threads = oracle.max_threads()
+    cu_k = np.array([0, L], dtype=np.int32)
+    m, t_used, flops, rows = 4, 0.0, 0, 0
+    while t_used < seconds and m <= L:
+        cu_q = np.array([0, m], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.attn_backward(q[L - m:L], k[:L], v[:L], do_cpu[L - m:L], cu_q, w.n_heads_q,
+                             w.n_heads_kv, route, w.sink, w.window, cu_seqlens_k=cu_k,
+                             nthreads=threads)
+        t_used += time.perf_counter() - t0
+        flops += metrics.chunk_flops([L], [m], route.tolist(), w.head_dim, w.sink,
+                                     w.window) * 5 // 2
+        rows += m
+        m *= 2
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"backward of the last 4..{m // 2} rows of the {L}-token sequence as chunks "
+                      f"over its prefix ({rows} rows x {w.n_heads_q} heads, {t_used:.1f} s of "
+                      f"fp64 oracle work); effective FLOPs as for the GPU"}
+
+
 def backward_main(args):
     """Training backward of the layer: the router's straight-through gradient
     (ea_route_backward) and the routed attention's dq, dk, dv (ea_hybrid_attn_backward), with
@@ -458,12 +491,12 @@ def backward_main(args):
     F = metrics.backward_flops(layer.lens, r, d, w.sink, w.window)
     f_dq, f_dkv = metrics.backward_kernel_flops(layer.lens, r, d, w.sink, w.window)
     value = F / (ms * 1e-3) / 1e12
-    valu_peak = metrics.MI355X_FP32_VECTOR_TFLOPS
+    peak = metrics.MI355X_BF16_DENSE_TFLOPS
     kern_tf = (f_dq + f_dkv) / (ms_attn * 1e-3) / 1e12
     rec = {
         "metric": BACKWARD_METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + "_backward", "batch": B, "seq_len": layer.max_len,
                    "n_heads_q": hq, "n_heads_kv": w.n_heads_kv, "head_dim": d, "sink": w.sink,
@@ -472,14 +505,23 @@ def backward_main(args):
                    "inputs": "bf16", "gradients": "fp32"},
         "effective_tflop": round(F / 1e12, 4),
         "attn_backward_ms": round(ms_attn, 4), "route_backward_ms": round(ms_route, 4),
-        "roofline": {"bound": "alu", "kernel": "bwd_dq_kernel + bwd_dkv_kernel (fp32 VALU)",
-                     "achieved": round(kern_tf, 2), "peak": valu_peak, "unit": "TFLOP/s",
-                     "frac": round(kern_tf / valu_peak, 4), "traffic": None,
+        "roofline": {"bound": "mfma",
+                     "kernel": "ea_hybrid_attn_backward (bwd_dq_mfma<128> + bwd_dkv_mfma<128>)",
+                     "achieved": round(kern_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kern_tf / peak, 4),
+                     "traffic": measured_traffic(w.name + "_backward", BWD_TRAFFIC_FILE,
+                                                 BWD_SOURCE),
                      "launch_ms": round(ms_attn, 4),
-                     "note": "launch_ms is the whole ea_hybrid_attn_backward call (D, dq, dk/dv "
-                             "launches); achieved counts 6*D (dq) + 8*D (dk/dv) FLOPs per kept "
-                             "position and head"},
+                     "note": "launch_ms is the whole ea_hybrid_attn_backward call (D, dq, dk/dv, "
+                             "partial reduce); achieved counts the products the two matrix-core "
+                             "kernels run per kept position and head: 6*D (dq: S, dP, dQ) + "
+                             "8*D (dk/dv: S, dP, dV, dK); traffic is the dk/dv kernel's"},
     }
+    if args.copy_calibration:
+        copy_calibration()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        rec["cpu_baseline"] = backward_cpu_baseline(layer, inputs.dout(w, T), args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 
