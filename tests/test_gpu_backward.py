@@ -277,3 +277,60 @@ def test_route_backward_workload_shape():
         S = max(1.0, float(np.abs(r).max()))
         say(f"  {name}: max_abs {err.max():.3e} scale {S:.3e}")
         assert err.max() <= 1e-5 * S, name
+
+
+def test_backward_workload_32k_sampled():
+    """The Qwen3-8B-shaped 32K layer as bench.py runs it (router routing, bf16): sampled dq
+    rows against one-row oracle chunks (exact for the row), dk and dv of the last 64 keys
+    against the oracle backward of the last 64 rows as a chunk (every row that sees those keys
+    is in it), and for every key the identities sum_j dk_j = 0 and sum_j dv_j = sum over rows
+    and group heads of dO (softmax rows sum to one)."""
+    import json
+    import os
+    w = inputs.WORKLOADS["qwen3_8b_32k"]
+    L = w.lengths[0]
+    hq, hkv, d = w.n_heads_q, w.n_heads_kv, w.head_dim
+    G = hq // hkv
+    dev = H.device()
+    q, k, v = inputs.qkv(w, L)
+    do = inputs.dout(w, L)
+    cu = inputs.cu_seqlens([L])
+    w1, b1, w2, b2 = inputs.router_weights(w)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "router_bias_qwen3_8b_32k.json")) as f:
+        b2 = torch.full_like(b2, json.load(f)["b2"])
+    ks = k.view(L, hkv * d)
+    route = torch.empty(1, hq, dtype=torch.uint8, device=dev)
+    ws = H.workspace(1, L, hq, ks.shape[1], w1.shape[0])
+    ea.route(H.to_gpu(ks), H.to_gpu(cu), H.to_gpu(w1), H.to_gpu(b1), H.to_gpu(w2), H.to_gpu(b2),
+             route, ws)
+    torch.cuda.synchronize()
+    route = route.cpu()
+    say(f"case backward 32K workload: sparse heads {int(route.sum())}")
+    o, lse, _, _ = H.run_prefill(q, k, v, [L], route, w.sink, w.window, worklist=False)
+    dq, dk, dv = run_backward(q, k, v, o, do, lse, cu, route, w.sink, w.window)
+    r = route.numpy()
+    # sampled dq rows: boundaries of the sink and window and spread rows
+    rows = sorted({0, 1, w.sink - 1, w.sink, w.window - 1, w.window, w.sink + w.window - 1,
+                   w.sink + w.window, 5000, 12345, 20000, 27777, L - 2, L - 1})
+    for i in rows:
+        rq, _, _ = oracle.attn_backward(q[i:i + 1], k[:i + 1], v[:i + 1], do[i:i + 1],
+                                        inputs.cu_seqlens([1]), hq, hkv, r, w.sink, w.window,
+                                        cu_seqlens_k=inputs.cu_seqlens([i + 1]))
+        check_grad(dq[i:i + 1], rq, torch.bfloat16, f"dq row {i}")
+    # dk, dv of the last 64 keys
+    m = 64
+    _, rk, rv = oracle.attn_backward(q[L - m:], k, v, do[L - m:], inputs.cu_seqlens([m]), hq,
+                                     hkv, r, w.sink, w.window,
+                                     cu_seqlens_k=inputs.cu_seqlens([L]))
+    check_grad(dk[L - m:], rk[L - m:], torch.bfloat16, "dk last 64 keys")
+    check_grad(dv[L - m:], rv[L - m:], torch.bfloat16, "dv last 64 keys")
+    # column identities over every key, per KV head
+    sk = dk.double().sum(dim=0)                            # [hkv, d]
+    sv = dv.double().sum(dim=0)
+    want_v = do.double().sum(dim=0).view(hkv, G, d).sum(dim=1)
+    abs_k = dk.double().abs().sum(dim=0)
+    err_k = float((sk.abs() / abs_k.clamp_min(1e-30)).max())
+    err_v = float(((sv - want_v).abs() / do.double().abs().sum(dim=0).view(hkv, G, d).sum(dim=1)).max())
+    say(f"  sum dk relative {err_k:.3e}, sum dv relative {err_v:.3e}")
+    # bf16 P and dS operands: each term is within 2^-8 relative of the exact one
+    assert err_k <= 2e-3 and err_v <= 2e-3
