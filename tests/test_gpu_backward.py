@@ -334,3 +334,14 @@ def test_backward_workload_32k_sampled():
     say(f"  sum dk relative {err_k:.3e}, sum dv relative {err_v:.3e}")
     # bf16 P and dS operands: each term is within 2^-8 relative of the exact one
     assert err_k <= 2e-3 and err_v <= 2e-3
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 4, 64), (8, 1, 128), (16, 2, 64)])
+def test_backward_group_sizes(hq, hkv, d):
+    # one query head per KV head (dk, dv written directly, no partials) and large groups
+    # (partials of up to 8 heads summed in head order)
+    lens = [333, 700, 65]
+    g = torch.Generator().manual_seed(hq * 100 + hkv * 10 + d)
+    route = (torch.rand(len(lens), hq, generator=g) < 0.5).to(torch.uint8)
+    prefill_then_backward(lens, hq, hkv, d, torch.bfloat16, route, 8, 150, 60 + hq + hkv,
+                          f"groups hq{hq} hkv{hkv} d{d}")
