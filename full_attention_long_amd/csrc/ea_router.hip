@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void route_out(const float* __restrict__ hv, i
 //   route_bwd_hidden  du[b, j] = (sum_h dz[b, h] W2[h, j]) SiLU'(u[b, j]).
 //   route_bwd_w2      dW2[h, j] = sum_b dz[b, h] hs[b, j];  db2[h] = sum_b dz[b, h].
 //   route_bwd_w1      dW1[j, c] = sum_b du[b, j] x[b, c];  db1[j] = sum_b du[b, j].
-//   route_bwd_x       dx[b, c] = sum_j du[b, j] W1[j, c].
+//   route_bwd_x       dx[b, c] = sum_j du[b, j] W1[j, c] (hidden units split in four).
 //   route_bwd_spread  dkey_states[t, c] = dx[b, c] / n_b for the n_b rows t of sequence b.
 
 constexpr int kDrCols = 8;  // columns per thread in route_dr_partial
@@ -347,16 +347,23 @@ __global__ __launch_bounds__(256) void route_bwd_w1(const float* __restrict__ du
   }
 }
 
-// dx[b, c] (thread per c, blockIdx.y = b)
+// dx[b, c] (blockIdx.y = b): 64 columns per workgroup, its four wavefronts each summing a
+// quarter of the hidden units; the quarters are added in order (fixed, deterministic)
 __global__ __launch_bounds__(256) void route_bwd_x(const float* __restrict__ du,
                                                    const float* __restrict__ w1, int kv_dim,
                                                    int hidden, float* __restrict__ dx) {
-  const int b = blockIdx.y, c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= kv_dim) return;
+  __shared__ float part[4][64];
+  const int b = blockIdx.y, lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int j0 = hidden * q / 4, j1 = hidden * (q + 1) / 4;
   float s = 0.f;
-  for (int j = 0; j < hidden; ++j)
-    s = __builtin_fmaf(du[(int64_t)b * hidden + j], w1[(int64_t)j * kv_dim + c], s);
-  dx[(int64_t)b * kv_dim + c] = s;
+  if (c < kv_dim)
+    for (int j = j0; j < j1; ++j)
+      s = __builtin_fmaf(du[(int64_t)b * hidden + j], w1[(int64_t)j * kv_dim + c], s);
+  part[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && c < kv_dim)
+    dx[(int64_t)b * kv_dim + c] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
 }
 
 // dkey_states rows of sequence blockIdx.z, chunk blockIdx.x, columns 4 * thread of
@@ -446,8 +453,8 @@ hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t stream) {
       a.du, a.x, a.batch, a.kv_dim, a.hidden, a.dw1, a.db1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!a.dkey_states) return hipSuccess;
-  route_bwd_x<<<dim3((a.kv_dim + 255) / 256, a.batch), 256, 0, stream>>>(a.du, a.w1, a.kv_dim,
-                                                                         a.hidden, a.dx);
+  route_bwd_x<<<dim3((a.kv_dim + 63) / 64, a.batch), 256, 0, stream>>>(a.du, a.w1, a.kv_dim,
+                                                                       a.hidden, a.dx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   route_bwd_spread<<<dim3(a.dr_chunks, (a.kv_dim / 4 + 255) / 256, a.batch), 256, 0, stream>>>(
       a.dx, a.cu, a.kv_dim, a.dr_chunks, a.dkey_states);
