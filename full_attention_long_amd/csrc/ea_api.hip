@@ -825,8 +825,9 @@ ea_status ea_hybrid_attn_backward(
     return fail(EA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
   if (((uintptr_t)workspace & 255) != 0)
     return fail(EA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  if ((int64_t)max_seqlen_k * n_heads_kv * head_dim * 4 >= ((int64_t)1 << 31) ||
-      (int64_t)max_seqlen_k * n_heads_q * head_dim * 4 >= ((int64_t)1 << 31))
+  // the matrix-core kernels address one sequence's q / dO rows (all query heads; k and v are
+  // no larger) with 32-bit byte offsets; the fp32 kernels index with 64 bits
+  if (dt == EA_BF16 && (int64_t)max_seqlen_k * n_heads_q * head_dim * 2 > ((int64_t)1 << 31))
     return fail(EA_ERR_UNSUPPORTED, "sequence too long for 32-bit per-sequence addressing");
   if (!cu_seqlens_k) {
     cu_seqlens_k = cu_seqlens_q;

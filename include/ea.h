@@ -347,9 +347,9 @@ ea_status ea_hybrid_attn_decode_pool(const void* q, const void* k_pool, const vo
  *              element written (a key no row can see gets 0); they must not overlap the
  *              inputs or each other
  * head_dim 64 or 128; sink >= 0; window >= 1; scale <= 0 selects 1/sqrt(head_dim);
- * batch and n_heads_q at most 65535; all tensors 16-byte aligned; one sequence's rows of
- * q (or k) in fp32 below 2^31 bytes (max_seqlen_k * n_heads_q * head_dim * 4), else
- * EA_ERR_UNSUPPORTED
+ * batch and n_heads_q at most 65535; all tensors 16-byte aligned; for EA_BF16 one
+ * sequence's rows of q at most 2^31 bytes (max_seqlen_k * n_heads_q * head_dim * 2; 256K
+ * tokens at 32 x 128), else EA_ERR_UNSUPPORTED
  * workspace    ea_attn_backward_workspace_size(dt, batch, max_seqlen_q, max_seqlen_k,
  *              n_heads_q, n_heads_kv, head_dim) bytes, 256-byte aligned: the D_i values; for
  *              EA_BF16 also lse in base-2 units and, with several query heads per KV head, the

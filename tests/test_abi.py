@@ -352,6 +352,16 @@ def test_backward_host_checks():
     assert backward_call(cu_q_host=long_host) == ea.EA_ERR_INVALID_ARG
 
 
+def test_backward_sequence_length_limit():
+    # bf16: one sequence's q rows (all heads) must fit 2^31 bytes; 256K at 32 x 128 is the edge
+    big = dict(max_q=262145, max_k=262145, ws_bytes=1 << 40)
+    assert backward_call(**big) == ea.EA_ERR_UNSUPPORTED
+    # fp32 (64-bit indexing) has no such limit: the same sizes pass the host checks
+    if torch.cuda.device_count() == 0:
+        assert backward_call(dt=ea.EA_F32, **big) == ea.EA_ERR_HIP
+        assert backward_call(max_q=262144, max_k=262144, ws_bytes=1 << 40) == ea.EA_ERR_HIP
+
+
 def test_backward_workspace_size():
     f = ea.attn_backward_workspace_size
     a = f(ea.EA_F32, 2, 4096, 4096, 32, 8, 128)
