@@ -279,25 +279,31 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // bf16: the matrix-core kernels; fp32: the vector-ALU kernels below
-  if constexpr (sizeof(T) == 2) return launch_attn_backward_bf16_mfma(a, stream);
-  if (a.max_seqlen_q > 0) {  // no query rows: no dq, but dk = dv = 0 below
-    bwd_dq_kernel<T, D><<<dim3((a.max_seqlen_q + kBwdRows - 1) / kBwdRows, a.n_heads_q,
-                               a.batch),
-                          kBwdThreads, 0, stream>>>(a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    // bf16: the matrix-core kernels
+    return launch_attn_backward_bf16_mfma(a, stream);
+  } else {
+    // fp32: the vector-ALU kernels
+    if (a.max_seqlen_q > 0) {  // no query rows: no dq, but dk = dv = 0 below
+      bwd_dq_kernel<T, D><<<dim3((a.max_seqlen_q + kBwdRows - 1) / kBwdRows, a.n_heads_q,
+                                 a.batch),
+                            kBwdThreads, 0, stream>>>(a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    bwd_dkv_kernel<T, D><<<dim3((a.max_seqlen_k + kBwdRows - 1) / kBwdRows, a.n_heads_kv,
+                                a.batch),
+                           kBwdThreads, 0, stream>>>(a);
+    return hipGetLastError();
   }
-  bwd_dkv_kernel<T, D><<<dim3((a.max_seqlen_k + kBwdRows - 1) / kBwdRows, a.n_heads_kv, a.batch),
-                         kBwdThreads, 0, stream>>>(a);
-  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_backward(const BwdArgs& a, bool bf16, hipStream_t stream) {
   if (bf16)
-    return a.head_dim == 128 ? launch_bwd_t<__bf16, 128>(a, stream) : launch_bwd_t<__bf16, 64>(a, stream);
+    return a.head_dim == 128 ? launch_bwd_t<__bf16, 128>(a, stream)
+                             : launch_bwd_t<__bf16, 64>(a, stream);
   return a.head_dim == 128 ? launch_bwd_t<float, 128>(a, stream) : launch_bwd_t<float, 64>(a, stream);
 }
 
