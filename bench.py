@@ -48,6 +48,8 @@ ATTN_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_attn_bf1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_qwen3_8b_32k_traffic.json")
 DECODE_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_decode.hip")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_qwen3_8b_32k_traffic.json")
+DECODE_POOL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_pool_bf16_qwen3_8b_32k_traffic.json")
+CHUNK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_chunked_qwen3_8b_32k_chunk4096_traffic.json")
 BWD_SOURCE = os.path.join(ROOT, "full_attention_long_amd", "csrc", "ea_backward_bf16.hip")
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_backward_qwen3_8b_32k_traffic.json")
 
@@ -327,8 +329,9 @@ def decode_main(args, pooled=False):
                      "kernel": "decode_split_bf16_kernel<128,4> + decode_combine_kernel",
                      "achieved": round(gbps, 1), "peak": peak, "unit": "GB/s",
                      "frac": round(gbps / peak, 4),
-                     "traffic": None if pooled else measured_traffic(w.name, DECODE_TRAFFIC_FILE,
-                                                                     DECODE_SOURCE),
+                     "traffic": measured_traffic(
+                         w.name, DECODE_POOL_TRAFFIC_FILE if pooled else DECODE_TRAFFIC_FILE,
+                         DECODE_SOURCE),
                      "algorithmic_bytes": st.bytes, "launch_ms": round(ms, 5)},
     }
     if pooled:
@@ -392,9 +395,12 @@ def chunk_main(args):
         "effective_tflop": round(F / 1e12, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128>", "achieved": round(attn_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(attn_tf / peak, 4),
-                     "traffic": None, "launch_ms": round(ms_attn, 4),
+                     "traffic": measured_traffic(w.name + f"_chunk{Lq}", CHUNK_TRAFFIC_FILE),
+                     "launch_ms": round(ms_attn, 4),
                      "note": "launch_ms includes the planner launch"},
     }
+    if args.copy_calibration:
+        copy_calibration()
     print(json.dumps(rec), flush=True)
 
 
