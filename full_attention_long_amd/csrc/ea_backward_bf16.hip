@@ -9,19 +9,20 @@
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j.
 //
 // Two kernels (no atomics: every gradient element is written once, in a fixed order):
-//   * bwd_dkv_mfma: one workgroup per (128-key tile, query head, sequence), 4 wavefronts of
-//     32 keys.  K and V of the wavefront's keys stay in registers as the B operand of
-//     v_mfma_f32_32x32x16_bf16; for every 64-row stage of the rows that can see the tile (all
-//     later rows for a full head or a tile with sink keys, else the next window - 1
-//     positions), Q, dO, lse and D are staged in LDS and each wavefront runs, per 32-row
-//     sub-tile:
+//   * bwd_dkv_mfma: one workgroup per (128-key tile, query head, sequence), 8 wavefronts (4 key
+//     blocks of 32 keys x 2 row parities, two wavefronts per SIMD).  K and V of the tile sit in
+//     LDS as the B operand of v_mfma_f32_32x32x16_bf16; for every 64-row stage of the rows that
+//     can see the tile (all later rows for a full head or a tile with sink keys, else the next
+//     window - 1 positions), Q, dO, lse and D arrive in LDS by direct loads (double buffered)
+//     and each wavefront runs the 32-row sub-tile of its parity:
 //       S = Q K^T and dP = dO V^T   (lane: one key, 16 rows),
 //       P, dS on the vector ALU, rounded to bf16 as B operands,
 //       dV^T += dO^T P and dK^T += Q^T dS   (dO^T, Q^T read transposed from the row-major
 //       stage with ds_read_b64_tr_b16; rows permuted consistently on both operands).
-//     One query head per workgroup bounds the longest workgroup (a sink tile, or a tile of a
-//     full head) at one head's rows; with several query heads per KV head each writes fp32
-//     partials that bwd_dkv_reduce adds in head order (deterministic).
+//     The two parities add their partial sums through LDS in a fixed order.  One query head
+//     per workgroup bounds the longest workgroup (a sink tile, or a tile of a full head) at one
+//     head's rows; with several query heads per KV head each writes fp32 partials that
+//     bwd_dkv_reduce adds in head order (deterministic).
 //   * bwd_dq_mfma: one workgroup per (128-row q-tile, head, sequence), 4 wavefronts of 32
 //     rows, Q and dO of the wavefront's rows in registers; per 64-key tile of the forward's
 //     visit plan (sink tiles, then window or causal tiles), K and V staged in LDS:
@@ -32,8 +33,9 @@
 // the eight XCDs -- do not pin every tile of one head to one XCD.
 // LDS rows are XOR-swizzled per 16-byte chunk so that both the plain 16-byte reads (16
 // consecutive rows, one chunk) and the transposing 8-byte reads (4 aligned rows x 64 bytes)
-// hit distinct banks.  Rows past a sequence read as zero and carry lse = +inf (P = 0);
-// masks are applied only on sub-tiles that hide some pair.
+// hit distinct banks.  Rows and keys past a sequence read as zero; a row past the sequence
+// gets P = 0 (lse = +inf in dq, the masked path in dk/dv), and masks are applied only on
+// sub-tiles that hide some pair.
 #include <math.h>
 
 #include <type_traits>
@@ -101,15 +103,15 @@ __device__ __forceinline__ bf16x8 read_plain(const unsigned char* base, int R, i
 
 // ------------------------------------------------------------------------------ dk / dv
 
-// Products of one 32-row sub-tile in the dk/dv kernel, in groups of 4 MFMAs whose LDS operands
-// are read one group ahead (sched_barrier keeps the reads where they are issued):
-//   A groups (KSTEPS / 2): S += Q K^T and dP += dO V^T over two k-steps;
-//   C groups (DT): dV^T += dO^T P and dK^T += Q^T dS for one 16-row slice kh and two
-//   32-column tiles.
+// Products of one 32-row sub-tile in the dk/dv kernel (sched_barrier keeps each group's LDS
+// reads where they are issued):
+//   A groups (KSTEPS): S += Q K^T and dP += dO V^T over one k-step, the four operands (Q, dO
+//   rows; K, V of the key block) read one group ahead;
+//   C groups (NC = DT): dV^T += dO^T P and dK^T += Q^T dS for one 16-row slice kh and two
+//   32-column tiles, operands single-buffered (the partner wavefront covers the latency).
 template <int D>
 struct DkvOps {
   using S = BS<D>;
-  static constexpr int NA = S::KSTEPS / 2;
   static constexpr int NC = S::DT;
   static constexpr int HALF = S::DT / 2;  // column-tile pairs per 16-row slice
 };
