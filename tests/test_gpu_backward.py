@@ -345,3 +345,41 @@ def test_backward_group_sizes(hq, hkv, d):
     route = (torch.rand(len(lens), hq, generator=g) < 0.5).to(torch.uint8)
     prefill_then_backward(lens, hq, hkv, d, torch.bfloat16, route, 8, 150, 60 + hq + hkv,
                           f"groups hq{hq} hkv{hkv} d{d}")
+
+
+def test_backward_long_256k_sampled():
+    """The 256K long-context layer (Bernoulli routing, bf16): the largest sequence the bf16
+    kernels address (one sequence's q rows are 2^31 bytes).  Sampled dq rows against one-row
+    oracle chunks, dk and dv of the last 16 keys against the oracle chunk backward, and the
+    column identities for every key."""
+    w = inputs.WORKLOADS["long_256k"]
+    L = w.lengths[0]
+    hq, hkv, d = w.n_heads_q, w.n_heads_kv, w.head_dim
+    G = hq // hkv
+    q, k, v = inputs.qkv(w, L)
+    do = inputs.dout(w, L)
+    cu = inputs.cu_seqlens([L])
+    route = inputs.bernoulli_route(w, 1)
+    say(f"case backward 256K: sparse heads {int(route.sum())}")
+    o, lse, _, _ = H.run_prefill(q, k, v, [L], route, w.sink, w.window, worklist=False)
+    dq, dk, dv = run_backward(q, k, v, o, do, lse, cu, route, w.sink, w.window)
+    r = route.numpy()
+    for i in (0, w.sink, w.window + w.sink, 100000, 200001, L - 1):
+        rq, _, _ = oracle.attn_backward(q[i:i + 1], k[:i + 1], v[:i + 1], do[i:i + 1],
+                                        inputs.cu_seqlens([1]), hq, hkv, r, w.sink, w.window,
+                                        cu_seqlens_k=inputs.cu_seqlens([i + 1]))
+        check_grad(dq[i:i + 1], rq, torch.bfloat16, f"dq row {i}")
+    m = 16
+    _, rk, rv = oracle.attn_backward(q[L - m:], k, v, do[L - m:], inputs.cu_seqlens([m]), hq,
+                                     hkv, r, w.sink, w.window,
+                                     cu_seqlens_k=inputs.cu_seqlens([L]))
+    check_grad(dk[L - m:], rk[L - m:], torch.bfloat16, "dk last 16 keys")
+    check_grad(dv[L - m:], rv[L - m:], torch.bfloat16, "dv last 16 keys")
+    sk = dk.double().sum(dim=0)
+    sv = dv.double().sum(dim=0)
+    want_v = do.double().sum(dim=0).view(hkv, G, d).sum(dim=1)
+    err_k = float((sk.abs() / dk.double().abs().sum(dim=0).clamp_min(1e-30)).max())
+    err_v = float(((sv - want_v).abs() /
+                   do.double().abs().sum(dim=0).view(hkv, G, d).sum(dim=1)).max())
+    say(f"  sum dk relative {err_k:.3e}, sum dv relative {err_v:.3e}")
+    assert err_k <= 2e-3 and err_v <= 2e-3
