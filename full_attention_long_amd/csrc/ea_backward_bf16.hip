@@ -604,16 +604,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(BwdArgs a) {
   }
 }
 
-// dk, dv = sum over the G query heads of a KV head of their partials, in head order.
+// dk, dv = sum over the G query heads of a KV head of their partials, in head order; grid
+// (chunks, batch): the keys of sequence blockIdx.y, skipped as a whole when its packing breaks
+// the bounds the dk/dv kernel checks (then it wrote no partials, and dk, dv stay unwritten).
 __global__ __launch_bounds__(256) void bwd_dkv_reduce(BwdArgs a) {
-  const int Tk = a.cu_k[a.batch];
-  if (Tk < 0 || Tk > a.tk_cap) return;
+  const int b = blockIdx.y;
+  const int q0 = a.cu_q[b], Lq = a.cu_q[b + 1] - q0;
+  const int k0 = a.cu_k[b], Lk = a.cu_k[b + 1] - k0;
+  if (q0 < 0 || k0 < 0 || Lq > a.max_seqlen_q || Lk > a.max_seqlen_k || Lk < Lq ||
+      a.cu_q[a.batch] > a.tq_cap || a.cu_k[a.batch] > a.tk_cap || Lk <= 0)
+    return;
   const int G = a.n_heads_q / a.n_heads_kv;
-  const int64_t n4 = (int64_t)Tk * a.n_heads_kv * a.head_dim / 4;
-  const int64_t slice4 = a.tk_cap * a.n_heads_kv * a.head_dim / 4;
+  const int64_t row4 = (int64_t)a.n_heads_kv * a.head_dim / 4;  // float4 per key row
+  const int64_t i0 = (int64_t)k0 * row4, n4 = (int64_t)Lk * row4;
+  const int64_t slice4 = a.tk_cap * row4;
   const f32x4* kp = (const f32x4*)a.dk_part;
   const f32x4* vp = (const f32x4*)a.dv_part;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+  for (int64_t i = i0 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < i0 + n4;
+       i += (int64_t)gridDim.x * 256) {
     f32x4 sk = kp[i], sv = vp[i];
     for (int hh = 1; hh < G; ++hh) {
       sk += kp[hh * slice4 + i];
@@ -636,7 +644,8 @@ hipError_t launch_mfma(const BwdArgs& a, hipStream_t stream) {
   bwd_dkv_mfma<D><<<ktiles * a.n_heads_q * a.batch, kThreadsDkv, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_heads_q == a.n_heads_kv) return e;
-  bwd_dkv_reduce<<<2048, 256, 0, stream>>>(a);
+  const int chunks = (2048 + a.batch - 1) / a.batch;  // about 2048 workgroups in all
+  bwd_dkv_reduce<<<dim3(chunks, a.batch), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

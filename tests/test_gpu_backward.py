@@ -170,12 +170,13 @@ def test_backward_deterministic():
         assert torch.equal(x, y)
 
 
-def test_backward_device_packing_beyond_bounds():
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_device_packing_beyond_bounds(dtype):
     # without host copies, a sequence longer than max_seqlen_q is left unwritten; the others
-    # are computed as usual
+    # are computed as usual (bf16 with 2 query heads per KV head: the partial reduce too)
     lens = [100, 300]
     hq, hkv, d = 4, 2, 64
-    q, k, v, do = gen_inputs(lens, hq, hkv, d, torch.float32, 21)
+    q, k, v, do = gen_inputs(lens, hq, hkv, d, dtype, 21)
     route = torch.tensor([[0, 1, 0, 1], [1, 0, 1, 0]], dtype=torch.uint8)
     cu = inputs.cu_seqlens(lens)
     say("case backward packing beyond max_seqlen")
@@ -187,9 +188,9 @@ def test_backward_device_packing_beyond_bounds():
     assert torch.all(dv[100:] == sentinel)
     rq, rk, rv = oracle.attn_backward(q[:100], k[:100], v[:100], do[:100],
                                       inputs.cu_seqlens([100]), hq, hkv, route[:1].numpy(), 4, 32)
-    check_grad(dq[:100], rq, torch.float32, "in-bounds dq")
-    check_grad(dk[:100], rk, torch.float32, "in-bounds dk")
-    check_grad(dv[:100], rv, torch.float32, "in-bounds dv")
+    check_grad(dq[:100], rq, dtype, "in-bounds dq")
+    check_grad(dk[:100], rk, dtype, "in-bounds dk")
+    check_grad(dv[:100], rv, dtype, "in-bounds dv")
 
 
 # ----------------------------------------------------------------------------- router
