@@ -59,7 +59,7 @@ def gen_inputs(lens, hq, hkv, d, dtype, seed):
 
 
 def run_backward(q, k, v, o, do, lse, cu_q, route, sink, window, cu_k=None, max_q=None,
-                 max_k=None, host=True, sentinel=None):
+                 max_k=None, host=True, sentinel=None, scale=0.0):
     dev = H.device()
     lens_q = (cu_q[1:] - cu_q[:-1]).tolist()
     mq = max(lens_q) if max_q is None else max_q
@@ -78,20 +78,21 @@ def run_backward(q, k, v, o, do, lse, cu_q, route, sink, window, cu_k=None, max_
     ea.hybrid_attn_backward(
         H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), H.to_gpu(o), H.to_gpu(do), H.to_gpu(lse),
         H.to_gpu(cu_q), mq, H.to_gpu(route.to(torch.uint8).contiguous()), sink, window, dq, dk,
-        dv, ws, cu_seqlens_k=None if cu_k is None else H.to_gpu(cu_k), max_seqlen_k=mk,
+        dv, ws, scale=scale, cu_seqlens_k=None if cu_k is None else H.to_gpu(cu_k), max_seqlen_k=mk,
         cu_seqlens_q_host=cu_q.tolist() if host else None,
         cu_seqlens_k_host=(cu_k.tolist() if cu_k is not None else None) if host else None)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def prefill_then_backward(lens, hq, hkv, d, dtype, route, sink, window, seed, what):
+def prefill_then_backward(lens, hq, hkv, d, dtype, route, sink, window, seed, what, scale=0.0):
     q, k, v, do = gen_inputs(lens, hq, hkv, d, dtype, seed)
     cu = inputs.cu_seqlens(lens)
     say(f"case {what}: lens={lens} hq={hq} hkv={hkv} d={d} {dtype} sink={sink} window={window}")
-    o, lse, _, _ = H.run_prefill(q, k, v, lens, route, sink, window, worklist=False)
-    dq, dk, dv = run_backward(q, k, v, o, do, lse, cu, route, sink, window)
-    rq, rk, rv = oracle.attn_backward(q, k, v, do, cu, hq, hkv, route.numpy(), sink, window)
+    o, lse, _, _ = H.run_prefill(q, k, v, lens, route, sink, window, scale=scale, worklist=False)
+    dq, dk, dv = run_backward(q, k, v, o, do, lse, cu, route, sink, window, scale=scale)
+    rq, rk, rv = oracle.attn_backward(q, k, v, do, cu, hq, hkv, route.numpy(), sink, window,
+                                      scale=scale if scale > 0 else None)
     check_grad(dq, rq, dtype, f"{what} dq")
     check_grad(dk, rk, dtype, f"{what} dk")
     check_grad(dv, rv, dtype, f"{what} dv")
@@ -108,7 +109,7 @@ def test_backward_ragged(dtype, d):
     prefill_then_backward(lens, hq, hkv, d, dtype, route, 16, 200, 40 + d, f"ragged d{d}")
 
 
-@pytest.mark.parametrize("kind", ["full", "sparse", "w1_nosink", "window_covers"])
+@pytest.mark.parametrize("kind", ["full", "sparse", "w1_nosink", "w1_sink", "window_covers"])
 def test_backward_routing_edges(kind):
     lens = [640, 129]
     hq, hkv, d = 8, 2, 128
@@ -118,6 +119,8 @@ def test_backward_routing_edges(kind):
         route.zero_()
     elif kind == "w1_nosink":
         sink, window = 0, 1           # each row sees only itself
+    elif kind == "w1_sink":
+        sink, window = 16, 1          # each row sees the sink keys and itself
     elif kind == "window_covers":
         window = 4096                 # the sparse mask equals the causal one
     prefill_then_backward(lens, hq, hkv, d, torch.bfloat16, route, sink, window, 7, kind)
@@ -384,3 +387,48 @@ def test_backward_long_256k_sampled():
                    do.double().abs().sum(dim=0).view(hkv, G, d).sum(dim=1)).max())
     say(f"  sum dk relative {err_k:.3e}, sum dv relative {err_v:.3e}")
     assert err_k <= 2e-3 and err_v <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_custom_scale(dtype):
+    # a softmax scale other than 1/sqrt(D): it enters P (through the forward's LSE) and both
+    # dq and dk (scale * dS)
+    lens = [400, 77]
+    hq, hkv, d = 8, 2, 64
+    g = torch.Generator().manual_seed(5)
+    route = (torch.rand(len(lens), hq, generator=g) < 0.5).to(torch.uint8)
+    prefill_then_backward(lens, hq, hkv, d, dtype, route, 8, 100, 33, f"scale 0.07 {dtype}",
+                          scale=0.07)
+
+
+def test_backward_chunked_prefix_fp32():
+    # the fp32 kernels over a KV prefix (chunk rows at positions Lk - Lq + r)
+    lens_k, lens_q = [200, 513, 64], [200, 100, 1]
+    hq, hkv, d, sink, window = 4, 2, 64, 8, 90
+    g = torch.Generator().manual_seed(8)
+    Tk = sum(lens_k)
+    qfull = torch.randn(Tk, hq, d, generator=g)
+    k = torch.randn(Tk, hkv, d, generator=g)
+    v = torch.randn(Tk, hkv, d, generator=g)
+    cu_k = inputs.cu_seqlens(lens_k)
+    q = torch.cat([qfull[int(cu_k[b + 1]) - lq:int(cu_k[b + 1])] for b, lq in enumerate(lens_q)])
+    cu_q = inputs.cu_seqlens(lens_q)
+    do = torch.randn(q.shape, generator=g)
+    route = (torch.rand(len(lens_q), hq, generator=g) < 0.5).to(torch.uint8)
+    say(f"case chunked backward fp32: lens_k={lens_k} lens_q={lens_q}")
+    dev = H.device()
+    o = torch.empty(q.shape, dtype=q.dtype, device=dev)
+    lse = torch.empty((hq, q.shape[0]), dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.prefill_chunked_workspace_size(len(lens_q), max(lens_q), hq, d),
+                     dtype=torch.uint8, device=dev)
+    ea.hybrid_attn_prefill_chunked(H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), o, H.to_gpu(cu_q),
+                                   H.to_gpu(cu_k), max(lens_q), max(lens_k), H.to_gpu(route),
+                                   sink, window, ws, lse_out=lse)
+    torch.cuda.synchronize()
+    dq, dk, dv = run_backward(q, k, v, o.cpu(), do, lse.cpu(), cu_q, route, sink, window,
+                              cu_k=cu_k)
+    rq, rk, rv = oracle.attn_backward(q, k, v, do, cu_q, hq, hkv, route.numpy(), sink, window,
+                                      cu_seqlens_k=cu_k)
+    check_grad(dq, rq, torch.float32, "chunked fp32 dq")
+    check_grad(dk, rk, torch.float32, "chunked fp32 dk")
+    check_grad(dv, rv, torch.float32, "chunked fp32 dv")
