@@ -432,3 +432,24 @@ def test_backward_chunked_prefix_fp32():
     check_grad(dq, rq, torch.float32, "chunked fp32 dq")
     check_grad(dk, rk, torch.float32, "chunked fp32 dk")
     check_grad(dv, rv, torch.float32, "chunked fp32 dv")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_backward_random_configs(seed):
+    # seeded random shapes: lengths (empty and tile-ragged ones included), group size, head_dim,
+    # dtype, sink, window and routing all drawn
+    rng = np.random.default_rng(1000 + seed)
+    nseq = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.choice([0, 1, 31, 64, 97, 128, 200, 333, 513], size=nseq)]
+    if sum(lens) == 0:
+        lens[0] = 77
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    sink = int(rng.choice([0, 1, 4, 16, 64]))
+    window = int(rng.choice([1, 8, 50, 128, 1000]))
+    g = torch.Generator().manual_seed(seed)
+    route = (torch.rand(len(lens), hq, generator=g) < float(rng.random())).to(torch.uint8)
+    prefill_then_backward(lens, hq, hkv, d, dtype, route, sink, window, 200 + seed,
+                          f"random {seed}")
