@@ -92,6 +92,7 @@ def test_chunk_of_32k_sequence_sampled_rows():
     route = (torch.rand(1, hq, generator=g) < 0.85).to(torch.uint8)
     route[0, 0] = 0
     o, lse, _, _ = run_chunked(q, k, v, cu_q, cu_k, route, sink, window, worklist=False)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     rows = np.sort(np.random.default_rng(3).choice(lq, 512, replace=False))
     rows[0], rows[-1] = 0, lq - 1
     ro, rl = oracle.attn(q, k, v, cu_q, hq, hkv, route.numpy(), sink, window, rows=rows,
@@ -157,3 +158,36 @@ def test_device_lengths_beyond_max_seqlen_give_an_empty_work_list():
                                    route, 4, 64, wsc)
     torch.cuda.synchronize()
     assert torch.all(o.float() == -12288.0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_chunked_random_configs(seed):
+    """Seeded random chunks: 1-4 sequences, key lengths from 1 to 2600, chunk lengths from
+    empty to the whole sequence, group sizes 1-8, head_dim 64 or 128, bf16 or fp32, random
+    sink, window and routing; every chunk row and the work list against the oracle."""
+    rng = np.random.default_rng(3000 + seed)
+    nseq = int(rng.integers(1, 5))
+    lens_k = [int(x) for x in rng.choice([1, 64, 65, 300, 777, 1500, 2600], size=nseq)]
+    lens_q = [lk if rng.random() < 0.3 else int(rng.integers(0, lk + 1)) for lk in lens_k]
+    if sum(lens_q) == 0:
+        lens_q[0] = lens_k[0]
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    sink = int(rng.choice([0, 1, 16, 128]))
+    window = int(rng.choice([1, 50, 256, 3000]))
+    q, k, v, cu_q, cu_k = chunk_inputs(lens_k, lens_q, hq, hkv, d, dtype, 400 + seed)
+    g = torch.Generator().manual_seed(600 + seed)
+    route = (torch.rand(nseq, hq, generator=g) < float(rng.random())).to(torch.uint8)
+    say(f"case chunked random {seed}: lens_k={lens_k} lens_q={lens_q} hq={hq} hkv={hkv} d={d} "
+        f"{dtype} s={sink} W={window}")
+    o, lse, items, bm = run_chunked(q, k, v, cu_q, cu_k, route, sink, window)
+    ro, rl = oracle.attn(q, k, v, cu_q, hq, hkv, route.numpy(), sink, window, cu_seqlens_k=cu_k)
+    H.compare(o, ro, dtype, f"chunked random {seed}", strict=False)
+    tol = 4e-3 if dtype == torch.bfloat16 else 1e-5
+    assert np.abs(lse.double().numpy().T - rl).max() <= tol
+    _, bn = ea.tile_config(ea.dtype_code(dtype), d)
+    want = oracle.worklist(route.numpy(), cu_q, hq, sink, window, bm, bn, cu_seqlens_k=cu_k)
+    assert np.array_equal(items[:len(want)], want)
+    assert np.all(items[len(want):] == -1)

@@ -309,3 +309,25 @@ def test_pool_regions_that_cannot_serve_give_nan():
     for b, h in ((0, 2), (0, 3), (1, 0), (1, 1)):
         H.compare(o[b, h][None, None], ro[b, h][None, None], torch.bfloat16, f"valid {b},{h}",
                   strict=False)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_random_configs(seed):
+    """Seeded random decode batches: 1-8 sequences with lengths from 1 to the cache capacity,
+    group sizes 1-8, head_dim 64 or 128, bf16 or fp32, random sink, window and routing."""
+    rng = np.random.default_rng(4000 + seed)
+    B = int(rng.integers(1, 9))
+    cap = int(rng.choice([64, 300, 1024, 2100]))
+    lens = [int(rng.integers(1, cap + 1)) for _ in range(B)]
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    sink = int(rng.choice([0, 1, 16, 128]))
+    window = int(rng.choice([1, 50, 256, 3000]))
+    g = torch.Generator().manual_seed(500 + seed)
+    q = torch.randn(B, hq, d, generator=g).to(dtype)
+    kc = torch.randn(B, cap, hkv, d, generator=g).to(dtype)
+    vc = torch.randn(B, cap, hkv, d, generator=g).to(dtype)
+    route = (torch.rand(B, hq, generator=g) < float(rng.random())).to(torch.uint8)
+    check_decode(q, kc, vc, lens, route, sink, window, f"random {seed}")

@@ -42,6 +42,9 @@ def check_case(q, k, v, lens, route, sink, window, rows=None, what="", guard=0, 
     say(f"case {what}: lens={lens} hq={hq} hkv={hkv} d={q.shape[2]} {q.dtype} s={sink} W={window}")
     o, lse, items, guard_ok = H.run_prefill(q, k, v, lens, route, sink, window, guard=guard)
     assert guard_ok, "writes outside O"
+    # every row, compared or not, is finite; lse starts as NaN, so every entry was written
+    assert bool(torch.isfinite(o).all()), f"{what}: non-finite output"
+    assert bool(torch.isfinite(lse).all()), f"{what}: lse not finite or not written"
     cu = inputs.cu_seqlens(lens)
     ro, rlse = oracle.attn(q, k, v, cu, hq, hkv, route.numpy(), sink, window, rows=rows)
     sel = slice(None) if rows is None else torch.as_tensor(rows)
@@ -211,3 +214,25 @@ def test_router_ragged_with_empty_sequence(kdt):
     # bits must agree wherever the logit is not within float rounding of the threshold
     decided = np.abs(ref_z) > 1e-5
     assert np.array_equal(r.cpu().numpy()[decided], ref_r[decided])
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_random_configs(seed):
+    """Seeded random shapes: 1-5 sequences of mixed lengths (empty, one token, on and around
+    tile edges), group sizes 1-8, head_dim 64 or 128, bf16 or fp32, sink and window from the
+    degenerate to the covering, random routing; every row against the oracle."""
+    rng = np.random.default_rng(2000 + seed)
+    nseq = int(rng.integers(1, 6))
+    lens = [int(x) for x in rng.choice([0, 1, 2, 63, 64, 65, 255, 256, 257, 700, 1100], size=nseq)]
+    if sum(lens) == 0:
+        lens[0] = 129
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    sink = int(rng.choice([0, 1, 5, 64, 300]))
+    window = int(rng.choice([1, 7, 64, 333, 5000]))
+    q, k, v = rand_qkv(sum(lens), hq, hkv, d, dtype, 300 + seed)
+    g = torch.Generator().manual_seed(seed)
+    route = (torch.rand(len(lens), hq, generator=g) < float(rng.random())).to(torch.uint8)
+    check_case(q, k, v, lens, route, sink, window, what=f"random {seed}", strict=False)
