@@ -4,6 +4,7 @@
 // rejected call launches nothing and leaves every output untouched.  The library never
 // allocates device memory: the router partial sums, the planner's cells and the work
 // list live in the caller's workspace, carved by ws_layout().
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -49,20 +50,25 @@ bool tile_shape(ea_dtype dt, int32_t head_dim, int* bm, int* bn) {
 }
 
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];
+// per-device compute-unit count, filled on first use; calls from several host threads may
+// race to fill an entry, all with the same value, so relaxed atomics suffice
+std::atomic<int> g_cu_count[kMaxDevices];
 
 hipError_t cu_count(int* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices && g_cu_count[dev] > 0) {
-    *out = g_cu_count[dev];
-    return hipSuccess;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *out = cached;
+      return hipSuccess;
+    }
   }
   int n = 0;
   e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev] = n;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
   *out = n;
   return hipSuccess;
 }
