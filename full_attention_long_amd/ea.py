@@ -114,10 +114,17 @@ def _check(status: int):
 
 
 def _ptr(t):
+    """Device address of a tensor argument (a plain int passes through as an address).  The
+    library reads dense row-major buffers in GPU memory, so a host tensor or a strided view
+    raises here instead of being misread."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got strides {tuple(t.stride())}")
     return t.data_ptr()
 
 

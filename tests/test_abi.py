@@ -411,3 +411,12 @@ def test_route_backward_workspace_size():
     assert ea.route_backward_workspace_size(0, 1024, 256, 32, 128) == 0
     assert ea.route_backward_workspace_size(2, 1024, 256, 32, 128) < \
         ea.route_backward_workspace_size(4, 1024, 256, 32, 128)
+
+
+def test_binding_rejects_host_and_strided_tensors():
+    import torch
+    assert ea._ptr(None) is None and ea._ptr(1234) == 1234
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ea._ptr(torch.zeros(4, 4))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ea._ptr(torch.zeros(4, 4).t())
