@@ -128,6 +128,26 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _same(what, *ts, shape=True):
+    """The C calls take one dtype code and the sizes of the first tensor: the others must
+    match it (dtype, and shape unless shape=False), or the kernels would misread them or
+    write past their end."""
+    ts = [t for t in ts if t is not None and not isinstance(t, int)]
+    for t in ts[1:]:
+        if t.dtype != ts[0].dtype:
+            raise ValueError(f"{what}: dtypes differ ({ts[0].dtype} vs {t.dtype})")
+        if shape and tuple(t.shape) != tuple(ts[0].shape):
+            raise ValueError(f"{what}: shapes differ ({tuple(ts[0].shape)} vs {tuple(t.shape)})")
+
+
+def _qkvo(q, k, v, o):
+    _same("q, o", q, o)
+    _same("k, v", k, v)
+    _same("q, k", q, k, shape=False)
+    if k.shape[-1] != q.shape[-1]:
+        raise ValueError(f"head_dim differs: q {q.shape[-1]}, k {k.shape[-1]}")
+
+
 def _capacity(worklist):
     """Work-list capacity in items: rows of an int32 [n, 4] tensor."""
     if worklist is None or isinstance(worklist, int):
@@ -194,6 +214,7 @@ def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, wi
                         workspace, scale=0.0, cu_seqlens_host=None, lse_out=None,
                         worklist_out=None, stream=None):
     """ea_hybrid_attn_prefill: q/o [T, Hq, D], k/v [T, Hkv, D] (bf16 or fp32)."""
+    _qkvo(q, k, v, o)
     batch = cu_seqlens.numel() - 1
     host = None
     if cu_seqlens_host is not None:
@@ -211,6 +232,7 @@ def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, wi
 def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window, worklist,
                     n_items, workspace, scale=0.0, lse_out=None, grid_blocks=0, stream=None):
     """ea_hybrid_attn_run on a work list from build_worklist (n_items: device int32)."""
+    _qkvo(q, k, v, o)
     batch = cu_seqlens.numel() - 1
     _check(lib().ea_hybrid_attn_run(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype),
                                     _ptr(cu_seqlens), batch, max_seqlen, q.shape[1], k.shape[1],
@@ -230,6 +252,7 @@ def hybrid_attn_decode(q, k_cache, v_cache, o, seqlens, max_seqlen, route_bits, 
                        workspace, scale=0.0, seqlens_host=None, lse_out=None, stream=None):
     """ea_hybrid_attn_decode: q/o [B, Hq, D], k_cache/v_cache [B, cap, Hkv, D] (bf16 or fp32),
     seqlens [B] int32 device."""
+    _qkvo(q, k_cache, v_cache, o)
     batch = q.shape[0]
     host = None
     if seqlens_host is not None:
@@ -283,6 +306,7 @@ def hybrid_attn_decode_pool(q, k_pool, v_pool, o, seqlens, max_seqlen, n_heads_k
                             seqlens_host=None, lse_out=None, stream=None):
     """ea_hybrid_attn_decode_pool: q/o [B, Hq, D]; k_pool/v_pool [rows, D]; regions from
     decode_pool_layout (device copies)."""
+    _qkvo(q, k_pool, v_pool, o)
     batch = q.shape[0]
     host = None
     if seqlens_host is not None:
@@ -303,6 +327,7 @@ def hybrid_attn_prefill_chunked(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seql
                                 worklist_out=None, stream=None):
     """ea_hybrid_attn_prefill_chunked: q/o [Tq, Hq, D] (each sequence's last Lq positions),
     k/v [Tk, Hkv, D] packed by cu_seqlens_k."""
+    _qkvo(q, k, v, o)
     batch = cu_seqlens_q.numel() - 1
     hq = hk = None
     if cu_seqlens_q_host is not None:
@@ -338,6 +363,12 @@ def hybrid_attn_backward(q, k, v, o, dout, lse, cu_seqlens_q, max_seqlen_q, rout
                          stream=None):
     """ea_hybrid_attn_backward: q/o/dout [Tq, Hq, D], k/v [Tk, Hkv, D] (one dtype), lse
     [Hq, Tq] from the forward; dq/dk/dv fp32 outputs of the shapes of q/k/v."""
+    _qkvo(q, k, v, o)
+    _same("q, dout", q, dout)
+    _same("dq, dk, dv (fp32)", dq, dk, dv, shape=False)
+    _same("dk, dv", dk, dv)
+    if dq.dtype.itemsize != 4 or tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape):
+        raise ValueError("dq, dk, dv must be fp32 with the shapes of q, k, v")
     batch = cu_seqlens_q.numel() - 1
     if max_seqlen_k is None:
         max_seqlen_k = max_seqlen_q

@@ -420,3 +420,17 @@ def test_binding_rejects_host_and_strided_tensors():
         ea._ptr(torch.zeros(4, 4))
     with pytest.raises(ValueError, match="GPU tensor"):
         ea._ptr(torch.zeros(4, 4).t())
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    q = torch.zeros(8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(8, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    args = (cu, 8, torch.zeros(1, 4, dtype=torch.uint8), 0, 16, torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dtypes differ"):
+        ea.hybrid_attn_prefill(q, k, k.float(), q, *args)
+    with pytest.raises(ValueError, match="shapes differ"):
+        ea.hybrid_attn_prefill(q, k, k, q[:4], *args)
+    with pytest.raises(ValueError, match="head_dim differs"):
+        ea.hybrid_attn_prefill(q, k[..., :32], k[..., :32], q, *args)
