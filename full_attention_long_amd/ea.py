@@ -148,6 +148,17 @@ def _qkvo(q, k, v, o):
         raise ValueError(f"head_dim differs: q {q.shape[-1]}, k {k.shape[-1]}")
 
 
+def _arr(t, dtype, numel, what):
+    """A small device array argument: its dtype, and its element count where the call fixes it
+    (the library cannot see either)."""
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype != getattr(__import__("torch"), dtype):
+        raise ValueError(f"{what}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
+
+
 def _capacity(worklist):
     """Work-list capacity in items: rows of an int32 [n, 4] tensor."""
     if worklist is None or isinstance(worklist, int):
@@ -215,6 +226,9 @@ def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, wi
                         worklist_out=None, stream=None):
     """ea_hybrid_attn_prefill: q/o [T, Hq, D], k/v [T, Hkv, D] (bf16 or fp32)."""
     _qkvo(q, k, v, o)
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _arr(route_bits, "uint8", (cu_seqlens.numel() - 1) * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[1] * q.shape[0], "lse_out")
     batch = cu_seqlens.numel() - 1
     host = None
     if cu_seqlens_host is not None:
@@ -233,6 +247,9 @@ def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window
                     n_items, workspace, scale=0.0, lse_out=None, grid_blocks=0, stream=None):
     """ea_hybrid_attn_run on a work list from build_worklist (n_items: device int32)."""
     _qkvo(q, k, v, o)
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _arr(route_bits, "uint8", (cu_seqlens.numel() - 1) * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[1] * q.shape[0], "lse_out")
     batch = cu_seqlens.numel() - 1
     _check(lib().ea_hybrid_attn_run(_ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype),
                                     _ptr(cu_seqlens), batch, max_seqlen, q.shape[1], k.shape[1],
@@ -253,6 +270,9 @@ def hybrid_attn_decode(q, k_cache, v_cache, o, seqlens, max_seqlen, route_bits, 
     """ea_hybrid_attn_decode: q/o [B, Hq, D], k_cache/v_cache [B, cap, Hkv, D] (bf16 or fp32),
     seqlens [B] int32 device."""
     _qkvo(q, k_cache, v_cache, o)
+    _arr(seqlens, "int32", q.shape[0], "seqlens")
+    _arr(route_bits, "uint8", q.shape[0] * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[0] * q.shape[1], "lse_out")
     batch = q.shape[0]
     host = None
     if seqlens_host is not None:
@@ -307,6 +327,9 @@ def hybrid_attn_decode_pool(q, k_pool, v_pool, o, seqlens, max_seqlen, n_heads_k
     """ea_hybrid_attn_decode_pool: q/o [B, Hq, D]; k_pool/v_pool [rows, D]; regions from
     decode_pool_layout (device copies)."""
     _qkvo(q, k_pool, v_pool, o)
+    _arr(seqlens, "int32", q.shape[0], "seqlens")
+    _arr(route_bits, "uint8", q.shape[0] * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[0] * q.shape[1], "lse_out")
     batch = q.shape[0]
     host = None
     if seqlens_host is not None:
@@ -328,6 +351,10 @@ def hybrid_attn_prefill_chunked(q, k, v, o, cu_seqlens_q, cu_seqlens_k, max_seql
     """ea_hybrid_attn_prefill_chunked: q/o [Tq, Hq, D] (each sequence's last Lq positions),
     k/v [Tk, Hkv, D] packed by cu_seqlens_k."""
     _qkvo(q, k, v, o)
+    _arr(cu_seqlens_q, "int32", None, "cu_seqlens_q")
+    _arr(cu_seqlens_k, "int32", cu_seqlens_q.numel(), "cu_seqlens_k")
+    _arr(route_bits, "uint8", (cu_seqlens_q.numel() - 1) * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[1] * q.shape[0], "lse_out")
     batch = cu_seqlens_q.numel() - 1
     hq = hk = None
     if cu_seqlens_q_host is not None:
@@ -367,6 +394,10 @@ def hybrid_attn_backward(q, k, v, o, dout, lse, cu_seqlens_q, max_seqlen_q, rout
     _same("q, dout", q, dout)
     _same("dq, dk, dv (fp32)", dq, dk, dv, shape=False)
     _same("dk, dv", dk, dv)
+    _arr(cu_seqlens_q, "int32", None, "cu_seqlens_q")
+    _arr(cu_seqlens_k, "int32", cu_seqlens_q.numel(), "cu_seqlens_k")
+    _arr(route_bits, "uint8", (cu_seqlens_q.numel() - 1) * q.shape[1], "route_bits")
+    _arr(lse, "float32", q.shape[1] * q.shape[0], "lse")
     if dq.dtype.itemsize != 4 or tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape):
         raise ValueError("dq, dk, dv must be fp32 with the shapes of q, k, v")
     batch = cu_seqlens_q.numel() - 1

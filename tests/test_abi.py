@@ -434,3 +434,19 @@ def test_binding_rejects_mismatched_tensors():
         ea.hybrid_attn_prefill(q, k, k, q[:4], *args)
     with pytest.raises(ValueError, match="head_dim differs"):
         ea.hybrid_attn_prefill(q, k[..., :32], k[..., :32], q, *args)
+
+
+def test_binding_rejects_wrong_small_arrays():
+    import torch
+    q = torch.zeros(8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(8, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="route_bits: expected 4 elements"):
+        ea.hybrid_attn_prefill(q, k, k, q, cu, 8, torch.zeros(1, 3, dtype=torch.uint8), 0, 16, ws)
+    with pytest.raises(ValueError, match="cu_seqlens: expected int32"):
+        ea.hybrid_attn_prefill(q, k, k, q, cu.long(), 8, torch.zeros(1, 4, dtype=torch.uint8), 0,
+                               16, ws)
+    with pytest.raises(ValueError, match="lse_out: expected 32 elements"):
+        ea.hybrid_attn_prefill(q, k, k, q, cu, 8, torch.zeros(1, 4, dtype=torch.uint8), 0, 16, ws,
+                               lse_out=torch.zeros(4, 7))
