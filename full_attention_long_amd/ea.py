@@ -159,6 +159,18 @@ def _arr(t, dtype, numel, what):
         raise ValueError(f"{what}: expected {numel} elements, got {t.numel()}")
 
 
+def _router_shapes(key_states, w1, b1, w2, b2):
+    """w1 [H, C], b1 [H], w2 [Hq, H], b2 [Hq] fp32 with C the key-state width: the C call
+    takes C from key_states, H from w1 and Hq from w2, so the others must agree."""
+    C, Hh, Hq = key_states.shape[-1], w1.shape[0], w2.shape[0]
+    for t, want, what in ((w1, (Hh, C), "w1"), (b1, (Hh,), "b1"), (w2, (Hq, Hh), "w2"),
+                          (b2, (Hq,), "b2")):
+        _arr(t, "float32", None, what)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{what}: expected shape {want}, got {tuple(t.shape)}")
+    return Hq
+
+
 def _capacity(worklist):
     """Work-list capacity in items: rows of an int32 [n, 4] tensor."""
     if worklist is None or isinstance(worklist, int):
@@ -199,6 +211,10 @@ def route(key_states, cu_seqlens, w1, b1, w2, b2, route_out, workspace, logits_o
     """ea_route: key_states [T, C] (bf16/fp32), w1 [H, C], b1 [H], w2 [Hq, H], b2 [Hq] fp32;
     writes route_out [B, Hq] uint8 and optionally logits_out [B, Hq] fp32."""
     batch = cu_seqlens.numel() - 1
+    hq = _router_shapes(key_states, w1, b1, w2, b2)
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _arr(route_out, "uint8", batch * hq, "route_out")
+    _arr(logits_out, "float32", batch * hq, "logits_out")
     _check(lib().ea_route(_ptr(key_states), dtype_code(key_states.dtype), key_states.shape[-1],
                           _ptr(cu_seqlens), batch, _ptr(w1), _ptr(b1), w1.shape[0],
                           _ptr(w2), _ptr(b2), w2.shape[0], _ptr(logits_out), _ptr(route_out),
@@ -424,6 +440,21 @@ def route_backward(key_states, cu_seqlens, w1, b1, w2, b2, o_full, o_sparse, dou
     fp32 outputs dz [B, Hq], dw1 [H, C], db1 [H], dw2 [Hq, H], db2 [Hq], optional dr_out
     [B, Hq] and dkey_states [T, C]."""
     batch = cu_seqlens.numel() - 1
+    hq = _router_shapes(key_states, w1, b1, w2, b2)
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _same("o_full, o_sparse, dout", o_full, o_sparse, dout)
+    if dout.dim() != 3 or dout.shape[1] != hq or dout.shape[0] != key_states.shape[0]:
+        raise ValueError(f"dout: expected [{key_states.shape[0]}, {hq}, D], got {tuple(dout.shape)}")
+    for t, want, what in ((dz, (batch, hq), "dz"), (dw1, tuple(w1.shape), "dw1"),
+                          (db1, tuple(b1.shape), "db1"), (dw2, tuple(w2.shape), "dw2"),
+                          (db2, tuple(b2.shape), "db2"), (dr_out, (batch, hq), "dr_out"),
+                          (noise, (batch, hq), "noise"),
+                          (dkey_states, tuple(key_states.shape), "dkey_states")):
+        if t is None or isinstance(t, int):
+            continue
+        _arr(t, "float32", None, what)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{what}: expected shape {want}, got {tuple(t.shape)}")
     _check(lib().ea_route_backward(
         _ptr(key_states), dtype_code(key_states.dtype), key_states.shape[1], _ptr(cu_seqlens),
         batch, _ptr(w1), _ptr(b1), w1.shape[0], _ptr(w2), _ptr(b2), w2.shape[0], _ptr(o_full),

@@ -450,3 +450,18 @@ def test_binding_rejects_wrong_small_arrays():
     with pytest.raises(ValueError, match="lse_out: expected 32 elements"):
         ea.hybrid_attn_prefill(q, k, k, q, cu, 8, torch.zeros(1, 4, dtype=torch.uint8), 0, 16, ws,
                                lse_out=torch.zeros(4, 7))
+
+
+def test_binding_rejects_router_shape_mismatch():
+    import torch
+    ks = torch.zeros(8, 16, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    w1, b1 = torch.zeros(4, 16), torch.zeros(4)
+    w2, b2 = torch.zeros(3, 4), torch.zeros(3)
+    out, ws = torch.zeros(1, 3, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="w1: expected shape"):
+        ea.route(ks, cu, torch.zeros(4, 15), b1, w2, b2, out, ws)
+    with pytest.raises(ValueError, match="b2: expected shape"):
+        ea.route(ks, cu, w1, b1, w2, torch.zeros(4), out, ws)
+    with pytest.raises(ValueError, match="route_out: expected 3 elements"):
+        ea.route(ks, cu, w1, b1, w2, b2, torch.zeros(1, 2, dtype=torch.uint8), ws)
