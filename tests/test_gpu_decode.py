@@ -331,3 +331,40 @@ def test_decode_random_configs(seed):
     vc = torch.randn(B, cap, hkv, d, generator=g).to(dtype)
     route = (torch.rand(B, hq, generator=g) < float(rng.random())).to(torch.uint8)
     check_decode(q, kc, vc, lens, route, sink, window, f"random {seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pool_random_configs(seed):
+    """Seeded random pooled-cache steps: 1-8 sequences of lengths 1 up to the capacity, group
+    sizes 1-8, head_dim 64 or 128, bf16 or fp32, random sink, window and routing.  The pooled
+    step equals the dense-cache step bit for bit and the oracle within the bounds."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 9))
+    cap = int(rng.choice([64, 300, 1024, 2100]))
+    lens = [int(rng.integers(1, cap + 1)) for _ in range(B)]
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * G
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    sink = int(rng.choice([0, 1, 16, 128]))
+    window = int(rng.choice([1, 50, 256, 3000]))
+    g = torch.Generator().manual_seed(700 + seed)
+    q = torch.randn(B, hq, d, generator=g).to(dtype)
+    kc = torch.randn(B, cap, hkv, d, generator=g).to(dtype)
+    vc = torch.randn(B, cap, hkv, d, generator=g).to(dtype)
+    route = (torch.rand(B, hq, generator=g) < float(rng.random())).to(torch.uint8)
+    kp, vp, gb, gr, base, rows = build_pool(kc, vc, lens, route, sink, window, cap)
+    say(f"case pool random {seed}: B={B} cap={cap} lens={lens} hq={hq} hkv={hkv} d={d} {dtype} "
+        f"s={sink} W={window}")
+    o, lse = run_pool_decode(q, kp, vp, gb, gr, lens, route, hkv, sink, window)
+    od, ld = run_decode(q, kc, vc, lens, route, sink, window)
+    if dtype == torch.bfloat16:
+        assert torch.equal(o.view(torch.int16), od.view(torch.int16))
+    else:
+        assert torch.equal(o, od)
+    assert torch.equal(lse, ld)
+    ro, rl = oracle.decode(q, kc, vc, lens, hkv, route.numpy(), sink, window)
+    H.compare(o, ro, dtype, f"pool random {seed}", strict=False)
+    tol = 1e-3 if dtype == torch.bfloat16 else 1e-5
+    assert np.abs(lse.double().numpy() - rl).max() <= tol
