@@ -34,6 +34,12 @@ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// A window longer than every sequence hides nothing: clamping it to max_len + 1 keeps the
+// mask and keeps the kernels' position arithmetic (i - window, j + window) inside 32 bits.
+int32_t clamp_window(int32_t window, int64_t max_len) {
+  return (int32_t)(window < max_len + 1 ? window : max_len + 1);
+}
+
 bool tile_shape(ea_dtype dt, int32_t head_dim, int* bm, int* bn) {
   if (head_dim != 64 && head_dim != 128) return false;
   if (dt == EA_BF16) {
@@ -87,12 +93,14 @@ ea_status check_plan_limits(int32_t batch, int32_t max_seqlen, int32_t n_heads_q
   return EA_OK;
 }
 
-// Checks shared by the attention entry points.  Fills bm/bn.
+// Checks shared by the attention entry points.  Fills bm/bn.  max_seqlen bounds the key
+// sequences (32-bit per-sequence addressing); plan_seqlen bounds the query rows the planner
+// tiles (the chunk length of a chunked prefill, else max_seqlen).
 ea_status check_attn_args(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
                           const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                           int32_t n_heads_q, int32_t n_heads_kv, int32_t head_dim,
                           const uint8_t* route, int32_t sink, int32_t window, float scale,
-                          void* workspace, int* bm, int* bn) {
+                          void* workspace, int* bm, int* bn, int32_t plan_seqlen = -1) {
   if (!q || !k || !v || !o || !cu_seqlens || !route || !workspace)
     return fail(EA_ERR_INVALID_ARG, "null pointer argument");
   if (dt != EA_BF16 && dt != EA_F32) return fail(EA_ERR_INVALID_ARG, "unknown dtype");
@@ -111,7 +119,7 @@ ea_status check_attn_args(const void* q, const void* k, const void* v, void* o, 
   if ((int64_t)max_seqlen * n_heads_kv * head_dim * elem >= ((int64_t)1 << 31) ||
       (int64_t)(*bm + 1) * n_heads_q * head_dim * elem >= ((int64_t)1 << 31))
     return fail(EA_ERR_UNSUPPORTED, "sequence too long for 32-bit per-sequence addressing");
-  return check_plan_limits(batch, max_seqlen, n_heads_q, *bm);
+  return check_plan_limits(batch, plan_seqlen < 0 ? max_seqlen : plan_seqlen, n_heads_q, *bm);
 }
 
 ea_status check_cu_host(const int32_t* cu, int32_t batch, int32_t max_seqlen) {
@@ -260,10 +268,11 @@ bool ws_layout(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_
   size_t at = 0;
   L.counters = at;   at = align256(at + 16 * sizeof(int32_t));
   L.items = at;      at = align256(at + 16 * (size_t)L.item_cap);
-  // The router's scratch overlays the start of the workspace: it is dead once ea_route
-  // has written its bits, and calls that share a workspace are ordered on one stream.
+  // The router's scratch overlays the internal work list (not the counters, which must
+  // stay zero between calls): it is dead once ea_route has written its bits, and calls
+  // that share a workspace are ordered on one stream.
   L.router_chunks = router_chunks(batch);
-  size_t r = 0;
+  size_t r = L.items;
   L.router_partial = r;
   r = align256(r + sizeof(float) * (size_t)batch * L.router_chunks * (size_t)kv_dim);
   L.router_x = r;
@@ -375,6 +384,7 @@ ea_status ea_build_worklist(const uint8_t* route, const int32_t* cu_seqlens, int
     return fail(EA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   ea_status s = check_plan_limits(batch, max_seqlen, n_heads_q, bm);
   if (s != EA_OK) return s;
+  window = clamp_window(window, max_seqlen);
   if (worklist_capacity < item_bound(batch, max_seqlen, n_heads_q, bm))
     return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen / bm)");
   WsLayout L;
@@ -409,6 +419,7 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
                                 n_heads_kv, head_dim, route, sink, window, scale, workspace,
                                 &bm, &bn);
   if (s != EA_OK) return s;
+  window = clamp_window(window, max_seqlen);
   if (worklist_out && worklist_capacity < item_bound(batch, max_seqlen, n_heads_q, bm))
     return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen / bm)");
   if (cu_seqlens_host) {
@@ -449,11 +460,12 @@ ea_status ea_hybrid_attn_prefill_chunked(
   if (max_seqlen_q < 0 || max_seqlen_q > max_seqlen_k)
     return fail(EA_ERR_INVALID_ARG, "need 0 <= max_seqlen_q <= max_seqlen_k");
   int bm = 0, bn = 0;
-  // key windows are sized by max_seqlen_k (also the conservative bound for the planner)
+  // key windows are sized by max_seqlen_k; the planner tiles the chunk's max_seqlen_q rows
   ea_status s = check_attn_args(q, k, v, o, dt, cu_seqlens_q, batch, max_seqlen_k, n_heads_q,
                                 n_heads_kv, head_dim, route, sink, window, scale, workspace,
-                                &bm, &bn);
+                                &bm, &bn, max_seqlen_q);
   if (s != EA_OK) return s;
+  window = clamp_window(window, max_seqlen_k);
   if (o == k || o == v || q == k) return fail(EA_ERR_INVALID_ARG, "o aliases q, k or v");
   if (worklist_out && worklist_capacity < item_bound(batch, max_seqlen_q, n_heads_q, bm))
     return fail(EA_ERR_INVALID_ARG, "worklist_capacity below batch * n_heads_q * ceil(max_seqlen_q / bm)");
@@ -516,6 +528,7 @@ ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* 
                                 n_heads_kv, head_dim, route, sink, window, scale, workspace,
                                 &bm, &bn);
   if (s != EA_OK) return s;
+  window = clamp_window(window, max_seqlen);
   if (!worklist || !n_items) return fail(EA_ERR_INVALID_ARG, "null work list or item count");
   if (grid_blocks < 0) return fail(EA_ERR_INVALID_ARG, "grid_blocks < 0");
   if (worklist_capacity < 0) return fail(EA_ERR_INVALID_ARG, "worklist_capacity < 0");
@@ -581,6 +594,7 @@ ea_status ea_hybrid_attn_decode(const void* q, const void* k_cache, const void* 
   if (ws_bytes < need) return fail(EA_ERR_WORKSPACE, "workspace smaller than ea_decode_workspace_size()");
   const int64_t splits = ceil_div64(max_seqlen, kDecodeSplit);
   if (splits > 2147483647 / 2) return fail(EA_ERR_UNSUPPORTED, "too many splits");
+  window = clamp_window(window, max_seqlen);
   DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;
@@ -869,6 +883,7 @@ ea_status ea_hybrid_attn_backward(
   } else if (dq == dk || dq == dv || dk == dv) {
     return fail(EA_ERR_INVALID_ARG, "gradient buffers overlap");
   }
+  window = clamp_window(window, max_seqlen_k);
   BwdLayout WL;
   if (!bwd_layout(dt, batch, max_seqlen_q, max_seqlen_k, n_heads_q, n_heads_kv, head_dim, &WL))
     return fail(EA_ERR_INVALID_ARG, "sizes overflow the workspace layout");

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     if (tid == 0) s_item = atomicAdd(&a.queue[0], 1);
     __syncthreads();
     const int it = s_item;
-    if (it >= n_items) break;
+    if (it < 0 || it >= n_items) break;  // a corrupt queue head ends the loop too
     const int4 item = a.items[it];
     const int b = item.x, h = item.y, qt = item.z;
     // an item outside this call's sizes is skipped (the test is uniform across the

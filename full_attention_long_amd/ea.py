@@ -317,9 +317,29 @@ def decode_pool_layout(route_host, n_heads_kv, capacity, sink, window):
     return base, rows, int(total.value)
 
 
+def _pool_args(k, v, k_pool, v_pool, region_base, region_rows, route_bits, batch):
+    """The pool writers take the row size from k and the pool's row count from k_pool: the
+    pools must hold rows of k's dtype and head_dim, the region arrays one entry per
+    (sequence, KV head), or the kernels would write past the pool's end."""
+    _same("k, v", k, v)
+    _same("k_pool, v_pool", k_pool, v_pool)
+    _same("k, k_pool", k, k_pool, shape=False)
+    if k_pool.dim() != 2 or k_pool.shape[1] != k.shape[-1]:
+        raise ValueError(f"k_pool: expected [rows, {k.shape[-1]}], got {tuple(k_pool.shape)}")
+    n_regions = batch * k.shape[1]
+    _arr(region_base, "int64", n_regions, "region_base")
+    _arr(region_rows, "int32", n_regions, "region_rows")
+    _arr(route_bits, "uint8", None, "route_bits")
+    if route_bits is not None and not isinstance(route_bits, int) and route_bits.dim() == 2 \
+            and route_bits.shape[0] != batch:
+        raise ValueError(f"route_bits: expected {batch} rows, got {route_bits.shape[0]}")
+
+
 def decode_pool_fill(k, v, cu_seqlens, max_seqlen, n_heads_q, route_bits, sink, window,
                      region_base, region_rows, k_pool, v_pool, stream=None):
     """ea_decode_pool_fill: k/v [T, Hkv, D] packed by cu_seqlens into k_pool/v_pool [rows, D]."""
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _pool_args(k, v, k_pool, v_pool, region_base, region_rows, route_bits, cu_seqlens.numel() - 1)
     _check(lib().ea_decode_pool_fill(_ptr(k), _ptr(v), dtype_code(k.dtype), _ptr(cu_seqlens),
                                      cu_seqlens.numel() - 1, max_seqlen, n_heads_q, k.shape[1],
                                      k.shape[2], _ptr(route_bits), sink, window,
@@ -330,6 +350,9 @@ def decode_pool_fill(k, v, cu_seqlens, max_seqlen, n_heads_q, route_bits, sink, 
 def decode_pool_append(k_new, v_new, positions, n_heads_q, route_bits, sink, window,
                        region_base, region_rows, k_pool, v_pool, stream=None):
     """ea_decode_pool_append: k_new/v_new [B, Hkv, D] at positions [B] (int32 device)."""
+    _arr(positions, "int32", k_new.shape[0], "positions")
+    _pool_args(k_new, v_new, k_pool, v_pool, region_base, region_rows, route_bits,
+               k_new.shape[0])
     _check(lib().ea_decode_pool_append(_ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype),
                                        _ptr(positions), k_new.shape[0], n_heads_q, k_new.shape[1],
                                        k_new.shape[2], _ptr(route_bits), sink, window,

@@ -198,7 +198,10 @@ ea_status ea_hybrid_attn_prefill_chunked(
  * resident slot on the device); the output does not depend on it.
  * The workgroups take items through two queue counters kept in the workspace: they are
  * zeroed by ea_build_worklist and ea_hybrid_attn_prefill and left at zero by every
- * completed run, so pass a workspace that has been through one of those calls.
+ * completed run, so pass a workspace that has been through one of those calls.  No other
+ * entry point writes them (ea_route's scratch lies past them), so ea_route may run on the
+ * same workspace between ea_build_worklist and this call.  A queue head outside
+ * [0, n_items) ends every workgroup's loop: nothing is read outside the work list.
  */
 ea_status ea_hybrid_attn_run(const void* q, const void* k, const void* v, void* o, ea_dtype dt,
                              const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,

@@ -465,3 +465,46 @@ def test_binding_rejects_router_shape_mismatch():
         ea.route(ks, cu, w1, b1, w2, torch.zeros(4), out, ws)
     with pytest.raises(ValueError, match="route_out: expected 3 elements"):
         ea.route(ks, cu, w1, b1, w2, b2, torch.zeros(1, 2, dtype=torch.uint8), ws)
+
+
+def test_chunked_plan_limit_counts_chunk_rows():
+    """The planner tiles the chunk's rows, so its cell bound uses max_seqlen_q: 8 sequences
+    of 256K cached keys with 4K-row chunks pass every host check up to the workspace size
+    (2 * 8 * ceil(262144 / 256) cells would exceed the planner, 2 * 8 * 16 do not)."""
+    st = chunked_call(batch=8, max_q=4096, max_k=262144, ws_bytes=16)
+    assert st == ea.EA_ERR_WORKSPACE, ea.last_error()
+    need = ea.prefill_chunked_workspace_size(8, 4096, 32, 128)
+    assert need > 0
+    # beyond the planner's cells by the chunk rows themselves: still rejected
+    assert chunked_call(batch=8, max_q=262144, max_k=262144) == ea.EA_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_pool_mismatch():
+    """The pool writers take the row size from k and the row count from k_pool: a pool of
+    another dtype or width, or region arrays of the wrong type or length, are refused before
+    the C call (these tensors never reach the GPU)."""
+    import torch
+    B, hkv, d = 2, 2, 64
+    k = torch.zeros(5, hkv, d, dtype=torch.bfloat16)
+    kp = torch.zeros(40, d, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 3, 5], dtype=torch.int32)
+    route = torch.zeros(B, 4, dtype=torch.uint8)
+    base = torch.zeros(B * hkv, dtype=torch.int64)
+    rows = torch.zeros(B * hkv, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k, k_pool: dtypes differ"):
+        ea.decode_pool_fill(k.float(), k.float(), cu, 3, 4, route, 4, 16, base, rows, kp, kp)
+    with pytest.raises(ValueError, match="k_pool, v_pool: shapes differ"):
+        ea.decode_pool_fill(k, k, cu, 3, 4, route, 4, 16, base, rows, kp, kp[:20])
+    with pytest.raises(ValueError, match="k_pool: expected"):
+        ea.decode_pool_fill(k, k, cu, 3, 4, route, 4, 16, base, rows, kp[:, :32], kp[:, :32])
+    with pytest.raises(ValueError, match="region_base: expected int64"):
+        ea.decode_pool_fill(k, k, cu, 3, 4, route, 4, 16, base.int(), rows, kp, kp)
+    with pytest.raises(ValueError, match="region_rows: expected 4 elements"):
+        ea.decode_pool_fill(k, k, cu, 3, 4, route, 4, 16, base, rows[:3], kp, kp)
+    kn = torch.zeros(B, hkv, d, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="positions: expected int32"):
+        ea.decode_pool_append(kn, kn, torch.zeros(B, dtype=torch.int64), 4, route, 4, 16, base,
+                              rows, kp, kp)
+    with pytest.raises(ValueError, match="k, v: shapes differ"):
+        ea.decode_pool_append(kn, kn[:1], torch.zeros(B, dtype=torch.int32), 4, route, 4, 16,
+                              base, rows, kp, kp)

@@ -453,3 +453,22 @@ def test_backward_random_configs(seed):
     route = (torch.rand(len(lens), hq, generator=g) < float(rng.random())).to(torch.uint8)
     prefill_then_backward(lens, hq, hkv, d, dtype, route, sink, window, 200 + seed,
                           f"random {seed}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_window_of_int32_max_equals_full(dtype):
+    """window = 2^31 - 1 on every head: the gradients equal the full-attention ones (the
+    host clamps the window, so j + window stays inside 32 bits in the dk/dv row plan)."""
+    lens = [700, 129, 1]
+    hq, hkv, d = 8, 2, 128
+    q, k, v, do = gen_inputs(lens, hq, hkv, d, dtype, 23)
+    cu = inputs.cu_seqlens(lens)
+    route = torch.ones(len(lens), hq, dtype=torch.uint8)
+    big = 2**31 - 1
+    o, lse, _, _ = H.run_prefill(q, k, v, lens, route, 2, big, worklist=False)
+    dq, dk, dv = run_backward(q, k, v, o, do, lse, cu, route, 2, big)
+    full = np.zeros((len(lens), hq), np.uint8)
+    rq, rk, rv = oracle.attn_backward(q, k, v, do, cu, hq, hkv, full, 0, 1)
+    check_grad(dq, rq, dtype, "window 2^31-1 dq")
+    check_grad(dk, rk, dtype, "window 2^31-1 dk")
+    check_grad(dv, rv, dtype, "window 2^31-1 dv")

@@ -236,3 +236,51 @@ def test_prefill_random_configs(seed):
     g = torch.Generator().manual_seed(seed)
     route = (torch.rand(len(lens), hq, generator=g) < float(rng.random())).to(torch.uint8)
     check_case(q, k, v, lens, route, sink, window, what=f"random {seed}", strict=False)
+
+
+def test_worklist_route_run_share_a_workspace():
+    """ea_build_worklist, then ea_route, then ea_hybrid_attn_run on one workspace: the
+    router's scratch lies past the queue counters the run takes items through, so the run
+    still starts from a zero queue head and writes every row."""
+    lens = [700, 300]
+    hq, hkv, d = 8, 2, 128
+    q, k, v = rand_qkv(sum(lens), hq, hkv, d, torch.bfloat16, 31)
+    cu = inputs.cu_seqlens(lens)
+    g = torch.Generator().manual_seed(8)
+    C, Hh = hkv * d, 64
+    w1 = torch.randn(Hh, C, generator=g) * 0.05
+    b1 = torch.zeros(Hh)
+    w2 = torch.randn(hq, Hh, generator=g) * 0.05
+    b2 = torch.zeros(hq)
+    ks = k.reshape(sum(lens), C)
+    dcu, droute = H.to_gpu(cu), torch.empty(len(lens), hq, dtype=torch.uint8, device="cuda")
+    router = [H.to_gpu(t) for t in (ks, w1, b1, w2, b2)]
+    ws = H.workspace(len(lens), max(lens), hq, C, Hh)
+    ea.route(router[0], dcu, *router[1:], droute, ws)
+    wl = torch.empty(len(lens) * hq * 4, 4, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    ea.build_worklist(droute, dcu, max(lens), hq, 16, 128, ea.EA_BF16, d, wl, ws, n_items_out=cnt)
+    ea.route(router[0], dcu, *router[1:], droute, ws)   # the same bits, the scratch rewritten
+    o = torch.full((sum(lens), hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ea.hybrid_attn_run(H.to_gpu(q), H.to_gpu(k), H.to_gpu(v), o, dcu, max(lens), droute, 16, 128,
+                       wl, cnt, ws)
+    torch.cuda.synchronize()
+    route = droute.cpu()
+    ro, _ = oracle.attn(q, k, v, cu, hq, hkv, route.numpy(), 16, 128)
+    H.compare(o.cpu(), ro, torch.bfloat16, "build -> route -> run")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_window_of_int32_max_equals_full(dtype):
+    """window = 2^31 - 1 hides nothing: every sparse head equals a full head (the mask
+    arithmetic stays in 32 bits because the host clamps the window to the longest sequence)."""
+    lens = [513, 70, 300]
+    hq, hkv, d = 4, 2, 128
+    q, k, v = rand_qkv(sum(lens), hq, hkv, d, dtype, 17)
+    route = torch.ones(len(lens), hq, dtype=torch.uint8)
+    o, lse, _, _ = H.run_prefill(q, k, v, lens, route, 3, 2**31 - 1, worklist=False)
+    cu = inputs.cu_seqlens(lens)
+    ro, rlse = oracle.attn(q, k, v, cu, hq, hkv, np.zeros((len(lens), hq), np.uint8), 0, 1)
+    H.compare(o, ro, dtype, "window 2^31-1")
+    tol = 4e-3 if dtype == torch.bfloat16 else 1e-5
+    assert np.abs(lse.T.double().numpy() - rlse).max() <= tol
