@@ -14,7 +14,8 @@
 //     in its GEMM phase (P(t-1) V(t-1) then S(t) = K(t) Q^T, 32 MFMAs) the other is in its
 //     softmax phase (VALU), and the roles swap at every workgroup barrier.  Each SIMD
 //     holds one wavefront of each group, so its matrix core and its VALU work at the same
-//     time instead of one wavefront alternating between them.
+//     time instead of one wavefront alternating between them.  Each group has its own
+//     loop over the slots.
 //   * Persistent grid: each workgroup pops items from the longest-first work list with
 //     one atomic per item, so long full-head items start first and short sparse items
 //     fill the tail of the launch.  The last workgroup out re-zeroes the queue.
@@ -31,10 +32,14 @@
 //     per row so the b128 K reads (16 rows) and the transposing V reads (4 rows x 64 bytes
 //     per half-wavefront) hit distinct banks of the 64-bank LDS.
 //   * Softmax uses exp2 with log2(e) folded into the scale; all state is fp32.  P is
-//     taken relative to a per-row reference max and rounded to bf16; the row sums add
-//     the rounded values (v_dot2c_f32_bf16).  The reference only has to keep P <= 2^8,
-//     which a row sum <= 2^8 proves, so the row max, the O *= alpha pass and a recompute
-//     of P run only on the (rare) tiles where some lane's sum exceeds that bound.
+//     taken relative to a per-row reference max and rounded to bf16.  The row sums add
+//     the rounded values on the matrix core: one v_mfma_f32_16x16x32_bf16 per 16-key
+//     slice of P against a constant 0/1 selector, issued in the GEMM phase next to P V
+//     (the vector unit's dot2 runs on the matrix pipeline too, and waits behind the
+//     partner wavefront's MFMAs; the VALU keeps only what co-issues with them).  The
+//     reference only has to keep P <= 2^8, i.e. no score more than 8 / (scale log2 e)
+//     above it; a lane max over the tile (v_max3) checks that, and the row max, the O
+//     and l rescale run only on the (rare) tiles that fail it.
 //   * Masks are applied only on tiles that hide a pair of the wavefront's rows, in the
 //     cheapest form the tile needs: causal edge only, window edge only, or both.
 //   * Raw buffer loads/stores bound every access: keys past the sequence end read as
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);  // wave-uniform: group branches are scalar
   const int grp = wave >> 2;                  // ping-pong group: 0 = A, 1 = B
   const int row0 = 32 * wave;                 // first item row of this wavefront
   const int l32 = lane & 31, g = lane >> 5;
@@ -132,6 +137,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // V^T operand (ds_read_b64_tr_b16): source row/column inside a 16-key x 32-column block
   const int tr_row = 4 * g + (lane & 15) / 4;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Selector A operand of the row-sum MFMA (16x16x32): D[i][n] = sum over the four 8-key
+  // blocks of B, weighted by A[i][block].  B is a P operand, whose lane n + 16 blk holds
+  // query row n + 16 (blk % 2), keys of half blk / 2; output lane l holds D[4 (l / 16) + e]
+  // [l % 16] and owns query row l % 32 = l % 16 + 16 ((l / 16) % 2).  So A[i][blk] = 1 iff
+  // blk % 2 == (i / 4) % 2, and A's lane l (row l % 16, block l / 16) holds that for all 8
+  // elements: every output of lane l is the sum over both halves of its own row.
+  bf16x8 rsel;
+  {
+    const __bf16 one = (__bf16)((((lane >> 4) & 1) == ((lane >> 2) & 1)) ? 1.0f : 0.0f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rsel[e] = one;
+  }
 
   for (;;) {
     if (tid == 0) s_item = atomicAdd(&a.queue[0], 1);
@@ -144,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       // split-KV: the queue hands out pieces; piece `it` belongs to the last item whose first
       // piece is <= it
       const int v = it;
-      if (v >= min(*a.n_pieces, a.piece_prefix[n_items])) break;
+      if (v < 0 || v >= min(*a.n_pieces, a.piece_prefix[n_items])) break;
       int lo = 0, hi = n_items - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -153,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       it = uniform(lo);
       piece = uniform(v - a.piece_prefix[it]);
       n_pieces = uniform(a.piece_prefix[it + 1] - a.piece_prefix[it]);
-    } else if (it >= n_items) {
+    } else if (it < 0 || it >= n_items) {  // a corrupt queue head ends the loop too
       break;
     }
     const int4 item = a.items[it];
@@ -239,7 +256,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;  // reference max and lane-partial row sum
+    float m_ref = -INFINITY;  // reference max (score units), equal on both lanes of a row
+    float m_thr = -INFINITY;  // scores below m_ref + 8 / c_log2 give P < 2^8
+    float m_c = 0.f;          // the reference in exp2 units (0 while there is none)
+    // row sum of the bf16-rounded P: every lane holds its query row's sum four times
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
     f32x16 sacc[kSubN];   // S(t) from the GEMM phase, consumed by the softmax phase
     bf16x8 pb[kSubN][2];  // P(t) from the softmax phase, consumed by the next GEMM phase
 #pragma unroll
@@ -293,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int dt = 0; dt < S::DT; ++dt)
             oacc[dt] =
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[dt], pb[j][kh], oacc[dt], 0, 0, 0);
+          lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, pb[j][kh], lacc, 0, 0, 0);
         } else {
           const int j = (c - 4) / 2, k0 = KH * ((c - 4) % 2);
           if (k0 == 0)
@@ -321,15 +343,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     };
 
     // Softmax phase Y(t).  P(t) = exp2(S*c - m_ref*c) is taken relative to the row's
-    // reference max m_ref, rounded to bf16, and the row sum adds the rounded values
-    // (v_dot2c_f32_bf16 against ones), so numerator and denominator of the output use
-    // the same weights.  A row sum of at most 2^8 bounds every P of the row by 2^8 (P >= 0),
-    // which is all the reference max has to guarantee; only when a lane's sum exceeds it
-    // (or is not finite: no reference yet) does the wavefront take the exact path: row
-    // max, new reference max for every row, O and l rescaled, P recomputed.
-    auto compute_p = [&](float mc) -> float {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+    // reference max m_ref and rounded to bf16, the operand of P V and of the row sum.  The
+    // reference has to keep every P <= 2^8, i.e. every score below m_thr; only when some
+    // lane's tile max is not below it (or there is no reference yet) does the wavefront
+    // take the exact path: row max, new reference for every row, O and l rescaled.
+    auto compute_p = [&](float mc) {
 #pragma unroll
       for (int j = 0; j < kSubN; ++j)
 #pragma unroll
@@ -339,9 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           const bf16x2 w = {(__bf16)p0, (__bf16)p1};
           pb[j][r / 8][r % 8] = w[0];
           pb[j][r / 8][r % 8 + 1] = w[1];
-          ls[(r / 2) % 4] = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ls[(r / 2) % 4], false);
         }
-      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     auto softmax_phase = [&](int t) {
       const int kt = vis.tile(t);
@@ -382,31 +398,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
             sacc[j][r] = visible ? sacc[j][r] : -INFINITY;
           }
       }
-      float lt = compute_p(m_ref * c_log2);
-      if (__builtin_amdgcn_ballot_w64(!(lt <= 256.f)) != 0) {
-        // row max as a tree of 3-input maxima, then across the two lanes of the row
-        float mx[8];
+      // lane max of the tile: four chains of 3-input maxima
+      float mx[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int j = i / 4, r = 4 * (i % 4);
-          mx[i] = fmaxf(fmaxf(sacc[j][r], sacc[j][r + 1]), fmaxf(sacc[j][r + 2], sacc[j][r + 3]));
-        }
-        float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
-                         fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+      for (int q = 0; q < 4; ++q) {
+        const int j = q / 2, r = 8 * (q % 2);
+        float m = fmaxf(fmaxf(sacc[j][r], sacc[j][r + 1]), sacc[j][r + 2]);
+        m = fmaxf(fmaxf(m, sacc[j][r + 3]), sacc[j][r + 4]);
+        m = fmaxf(fmaxf(m, sacc[j][r + 5]), sacc[j][r + 6]);
+        mx[q] = fmaxf(m, sacc[j][r + 7]);
+      }
+      float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+      if (__builtin_amdgcn_ballot_w64(!(mt < m_thr)) != 0) {
+        // row max across the two lanes of the row
         mt = fmaxf(mt, xor32(mt));
         const float m_new = fmaxf(m_ref, mt);
         // alpha = 0 when there was no reference yet (O and l are still zero)
         const float alpha =
             m_new == m_ref ? 1.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * c_log2);
-        l_run *= alpha;
+        lacc *= alpha;
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
         m_ref = m_new;
-        lt = compute_p((m_ref == -INFINITY ? 0.f : m_ref) * c_log2);
+        m_thr = m_ref + 8.0f / c_log2;
+        m_c = (m_ref == -INFINITY ? 0.f : m_ref) * c_log2;
       }
-      l_run += lt;
+      compute_p(m_c);
     };
 
     // Slot schedule.  Tiles t = 0..N-1.  Group A runs X(t) in slot 2t and Y(t) in slot
@@ -416,61 +435,69 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     // freed by the barrier before.  Group B's next GEMM phase, one slot later, is the first
     // LDS read after its loads (the compiler waits for them there: the DMA writes may alias
     // any LDS read), and every odd slot ends with a full wait, so a load never stalls the
-    // GEMM phase of the slot that issued it.
+    // GEMM phase of the slot that issued it.  Each group runs its own loop over the slots
+    // (the wavefront index is uniform, so the split is a scalar branch): no slot picks one
+    // of two phases at run time, which keeps both loop bodies straight-line code that the
+    // register allocator handles without spills.
     const int N = vis.count;  // >= 1 for every valid item
     const std::true_type yes;
     const std::false_type no;
     // group B issues K(u+1) and V(u) at the start of slot 2u
     auto issue_loads = [&](int u) {
-      if (grp == 1) {
-        if (u + 1 < N) load_tile(kr, kbase + ((u + 1) & 1) * S::TILE_BYTES, vis.tile(u + 1), false);
-        load_tile(vr, vbase + (u & 1) * S::TILE_BYTES, vis.tile(u), true);
-      }
+      if (u + 1 < N) load_tile(kr, kbase + ((u + 1) & 1) * S::TILE_BYTES, vis.tile(u + 1), false);
+      load_tile(vr, vbase + (u & 1) * S::TILE_BYTES, vis.tile(u), true);
     };
-    auto slot_end = [&](int s) {
-      if (s & 1) {
-        __builtin_amdgcn_s_waitcnt(0);  // this slot's LDS reads and the loads of slot s-1
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads of this slot are done
-        __builtin_amdgcn_s_barrier();
-      }
+    auto end_even = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads of this slot are done
+      __builtin_amdgcn_s_barrier();
+    };
+    auto end_odd = [&]() {
+      __builtin_amdgcn_s_waitcnt(0);  // this slot's LDS reads and the loads of slot s-1
+      __syncthreads();
     };
     if (grp == 1) load_tile(kr, kbase, vis.tile(0), false);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // slots 0, 1: S(0) only (A then B); A runs Y(0) in slot 1
-    for (int s = 0; s < 2; ++s) {
-      if (s == 0) issue_loads(0);
-      if ((s & 1) == grp)
-        gemm_phase(0, no, yes);
-      else if (s == 1)
-        softmax_phase(0);
-      slot_end(s);
-    }
-    // steady state: slots 2 .. 2N-1, every GEMM phase runs P V and Q K^T
-    for (int s = 2; s < 2 * N; ++s) {
-      const int u = s >> 1;
-      if ((s & 1) == 0) issue_loads(u);
-      if ((s & 1) == grp)
+    // Each group runs its own slot sequence (2N + 2 slots, the same barriers): no slot
+    // chooses between the two phases, so each loop body is straight-line code.
+    if (grp == 0) {
+      // group A: X(u) in slot 2u, Y(u) in slot 2u+1
+      gemm_phase(0, no, yes);
+      end_even();
+      softmax_phase(0);
+      end_odd();
+      for (int u = 1; u < N; ++u) {
         gemm_phase(u, yes, yes);
-      else
-        softmax_phase(grp == 0 ? u : u - 1);
-      slot_end(s);
-    }
-    // slots 2N, 2N+1: the last P V (A then B); B runs Y(N-1) in slot 2N
-    for (int s = 2 * N; s < 2 * N + 2; ++s) {
-      if ((s & 1) == grp)
-        gemm_phase(N, yes, no);
-      else if ((s & 1) == 0)
-        softmax_phase(N - 1);
-      slot_end(s);
+        end_even();
+        softmax_phase(u);
+        end_odd();
+      }
+      gemm_phase(N, yes, no);
+      end_even();
+      end_odd();
+    } else {
+      // group B: Y(u-1) and the loads of K(u+1), V(u) in slot 2u, X(u) in slot 2u+1
+      issue_loads(0);
+      end_even();
+      gemm_phase(0, no, yes);
+      end_odd();
+      for (int u = 1; u < N; ++u) {
+        issue_loads(u);
+        softmax_phase(u - 1);
+        end_even();
+        gemm_phase(u, yes, yes);
+        end_odd();
+      }
+      softmax_phase(N - 1);
+      end_even();
+      gemm_phase(N, yes, no);
+      end_odd();
     }
 
     // ---- epilogue of a piece of a split item: unnormalised O, the row's reference max and
     // sum, in fp32, to the piece's slot (merged by the combine kernel)
     if (n_pieces > 1) {
-      const float l_tot = l_run + xor32(l_run);
+      const float l_tot = lacc[0];
       const int64_t slot = a.slot_base[it] + piece;
       const int row = row0 + l32;
       float* op = a.o_part + (slot * BM + row) * D;
@@ -490,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       continue;
     }
     // ---- epilogue: O = O / l, round to bf16, store this lane's query row
-    const float l_tot = l_run + xor32(l_run);
+    const float l_tot = lacc[0];
     const float inv = 1.0f / l_tot;
     const uint32_t row_off = (uint32_t)(row0 + l32) * q_row_bytes;
 #pragma unroll
