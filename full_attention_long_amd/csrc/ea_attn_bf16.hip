@@ -103,6 +103,17 @@ __device__ __forceinline__ Visit make_visit(bool sparse, int m0, int m1, int sin
   return v;
 }
 
+// make_rsrc on a base address and size the compiler is told are wavefront-uniform, so the
+// descriptor lives in scalar registers (a descriptor it takes for divergent is wrapped in a
+// loop over lanes at every buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -211,18 +222,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     // buffer windows: this item's Q/O rows of head h; this sequence's K/V of head kvh
     const int64_t qo_elem = ((int64_t)(seq0 + qt * BM) * Hq + h) * D;
     const uint32_t qo_bytes = (uint32_t)(m1 - m0 - 1) * q_row_bytes + D * 2;
-    const auto qr = make_rsrc((const __bf16*)a.q + qo_elem, qo_bytes);
-    const auto orr = make_rsrc((__bf16*)a.o + qo_elem, qo_bytes);
+    const auto qr = make_rsrc_u((const __bf16*)a.q + qo_elem, qo_bytes);
+    const auto orr = make_rsrc_u((__bf16*)a.o + qo_elem, qo_bytes);
     const int64_t kv_elem = ((int64_t)seq0k * Hkv + kvh) * D;
     const uint32_t kv_bytes = (uint32_t)(len_k - 1) * kv_row_bytes + D * 2;
-    const auto kr = make_rsrc((const __bf16*)a.k + kv_elem, kv_bytes);
-    const auto vr = make_rsrc((const __bf16*)a.v + kv_elem, kv_bytes);
+    const auto kr = make_rsrc_u((const __bf16*)a.k + kv_elem, kv_bytes);
+    const auto vr = make_rsrc_u((const __bf16*)a.v + kv_elem, kv_bytes);
 
     // Issue the direct-to-LDS loads of one K or V tile into a buffer.  Only the four
     // wavefronts of group B issue tile loads (in the slots where they run the softmax
     // phase, which reads no LDS); each fills LOADS groups of ROWS_PER_LOAD rows.
     auto load_tile = [&](const __amdgpu_buffer_rsrc_t& rs, unsigned char* dst, int kt,
-                         bool is_v) {
+                         bool is_v) __attribute__((always_inline)) {
       // the wavefront and tile indices are uniform; readfirstlane keeps the row offset
       // scalar (the compiler cannot prove it and would otherwise loop over lanes)
       const int wv = uniform(wave & 3);
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     // the compiler from sinking the reads next to their MFMAs), so one wavefront keeps
     // the matrix core busy on its own while its partner wavefront runs the softmax.
     // pv / qk: std::true_type or std::false_type (which of the two products to run)
-    auto gemm_phase = [&](int t, auto pv, auto qk) {
+    auto gemm_phase = [&](int t, auto pv, auto qk) __attribute__((always_inline)) {
       constexpr bool do_pv = decltype(pv)::value, do_qk = decltype(qk)::value;
       const unsigned char* vb = vbase + ((t - 1) & 1) * S::TILE_BYTES;
       const unsigned char* kb = kbase + (t & 1) * S::TILE_BYTES;
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       // stage c < 4: V^T operands of 16-key slice (j, kh) = (c / 2, c % 2), all column
       // tiles (P keys 32j + 16kh + 8(e/4) + 4g + e%4); stage c >= 4: K operands of
       // sub-tile j = (c - 4) / 2, k-steps KH*((c - 4) % 2) + [0, KH).
-      auto read_ops = [&](int c, bf16x8 (&op)[KH]) {
+      auto read_ops = [&](int c, bf16x8 (&op)[KH]) __attribute__((always_inline)) {
         if (c < 4) {
           const int j = c / 2, kh = c % 2;
           const int row = 32 * j + 16 * kh + tr_row;
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         }
       };
       // sacc[j][r] = score(key kt*BN + 32j + 8(r/4) + 4g + r%4, query qi)
-      auto run_ops = [&](int c, const bf16x8 (&op)[KH]) {
+      auto run_ops = [&](int c, const bf16x8 (&op)[KH]) __attribute__((always_inline)) {
         if (c < 4) {
           const int j = c / 2, kh = c % 2;
 #pragma unroll
@@ -347,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     // reference has to keep every P <= 2^8, i.e. every score below m_thr; only when some
     // lane's tile max is not below it (or there is no reference yet) does the wavefront
     // take the exact path: row max, new reference for every row, O and l rescaled.
-    auto compute_p = [&](float mc) {
+    auto compute_p = [&](float mc) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < kSubN; ++j)
 #pragma unroll
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           pb[j][r / 8][r % 8 + 1] = w[1];
         }
     };
-    auto softmax_phase = [&](int t) {
+    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
       const int kt = vis.tile(t);
       const int k0 = kt * BN;
       // hidden pairs in this tile for this wavefront's rows: past the diagonal (or past
@@ -443,15 +454,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const std::true_type yes;
     const std::false_type no;
     // group B issues K(u+1) and V(u) at the start of slot 2u
-    auto issue_loads = [&](int u) {
+    auto issue_loads = [&](int u) __attribute__((always_inline)) {
       if (u + 1 < N) load_tile(kr, kbase + ((u + 1) & 1) * S::TILE_BYTES, vis.tile(u + 1), false);
       load_tile(vr, vbase + (u & 1) * S::TILE_BYTES, vis.tile(u), true);
     };
-    auto end_even = [&]() {
+    auto end_even = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS reads of this slot are done
       __builtin_amdgcn_s_barrier();
     };
-    auto end_odd = [&]() {
+    auto end_odd = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_s_waitcnt(0);  // this slot's LDS reads and the loads of slot s-1
       __syncthreads();
     };
