@@ -6,6 +6,7 @@
 // list live in the caller's workspace, carved by ws_layout().
 #include <atomic>
 #include <math.h>
+#include <mutex>
 #include <string.h>
 
 #include <string>
@@ -302,9 +303,71 @@ bool ws_layout_split(int32_t batch, int32_t max_seqlen_q, int32_t n_heads_q, int
 
 }  // namespace ea
 
+namespace ea {
+namespace {
+
+// Device-resident workspace of ea_hybrid_attn_prefill_noalloc: the queue counters and the
+// internal work list, for callers that cannot allocate.  Every GPU the library runs on
+// holds its own copy until the process ends; all calls on one GPU share it.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The array's device address on each device, taken once with that device current (the
+// host-side name of a __device__ array is a stand-in, not a device address).
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+}  // namespace ea
+
 using namespace ea;
 
 extern "C" {
+
+ea_status ea_hybrid_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
+                                         ea_dtype dt, const int32_t* cu_seqlens,
+                                         const int32_t* cu_seqlens_host, int32_t batch,
+                                         int32_t max_seqlen, int32_t n_heads_q,
+                                         int32_t n_heads_kv, int32_t head_dim,
+                                         const uint8_t* route, int32_t sink, int32_t window,
+                                         float scale, float* lse_out, int32_t* worklist_out,
+                                         int64_t worklist_capacity, void* stream) {
+  g_last_error.clear();
+  WsLayout L;
+  if (batch < 1 || max_seqlen < 0 || n_heads_q < 1 ||
+      !ws_layout(batch, max_seqlen, n_heads_q, 0, 0, &L))
+    return fail(EA_ERR_INVALID_ARG, "batch < 1, max_seqlen < 0, n_heads_q < 1 or sizes overflow");
+  if (L.total > kNoAllocScratchBytes)
+    return fail(EA_ERR_UNSUPPORTED,
+                "the work list needs " + std::to_string(L.total) +
+                    " bytes; the no-allocation entry point holds 4194304 (batch * n_heads_q * "
+                    "ceil(max_seqlen / 64) <= 262128)");
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "device scratch address");
+  // the planner launched by the call below zeroes the queue counters before the
+  // attention kernel reads them, so nothing left by an earlier call is read
+  return ea_hybrid_attn_prefill(q, k, v, o, dt, cu_seqlens, cu_seqlens_host, batch, max_seqlen,
+                                n_heads_q, n_heads_kv, head_dim, route, sink, window, scale,
+                                lse_out, worklist_out, worklist_capacity, ws,
+                                kNoAllocScratchBytes, stream);
+}
 
 size_t ea_workspace_size(int32_t batch, int32_t max_seqlen, int32_t n_heads_q, int32_t kv_dim,
                          int32_t hidden) {

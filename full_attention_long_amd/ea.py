@@ -23,7 +23,8 @@ EXPORTS = ("ea_workspace_size", "ea_tile_config", "ea_status_string", "ea_last_e
            "ea_decode_pool_fill", "ea_decode_pool_append", "ea_hybrid_attn_decode_pool",
            "ea_hybrid_attn_prefill_chunked", "ea_prefill_chunked_workspace_size",
            "ea_attn_backward_workspace_size", "ea_hybrid_attn_backward",
-           "ea_route_backward_workspace_size", "ea_route_backward")
+           "ea_route_backward_workspace_size", "ea_route_backward",
+           "ea_hybrid_attn_prefill_noalloc")
 
 _lib = None
 
@@ -61,6 +62,9 @@ def lib():
     L.ea_hybrid_attn_prefill.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, P,
                                          i32, i32, f32, P, P, i64, P, sz, P]
     L.ea_hybrid_attn_prefill.restype = i32
+    L.ea_hybrid_attn_prefill_noalloc.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, i32, i32,
+                                                 P, i32, i32, f32, P, P, i64, P]
+    L.ea_hybrid_attn_prefill_noalloc.restype = i32
     L.ea_hybrid_attn_run.argtypes = [P, P, P, P, i32, P, i32, i32, i32, i32, i32, P, i32, i32,
                                      f32, P, P, i64, P, i32, P, sz, P]
     L.ea_hybrid_attn_run.restype = i32
@@ -257,6 +261,26 @@ def hybrid_attn_prefill(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, wi
                                         _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream)))
+
+
+def hybrid_attn_prefill_noalloc(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window,
+                                scale=0.0, cu_seqlens_host=None, lse_out=None, worklist_out=None,
+                                stream=None):
+    """ea_hybrid_attn_prefill_noalloc: ea_hybrid_attn_prefill without a workspace argument
+    (the library's device-resident scratch; the call allocates nothing)."""
+    _qkvo(q, k, v, o)
+    _arr(cu_seqlens, "int32", None, "cu_seqlens")
+    _arr(route_bits, "uint8", (cu_seqlens.numel() - 1) * q.shape[1], "route_bits")
+    _arr(lse_out, "float32", q.shape[1] * q.shape[0], "lse_out")
+    batch = cu_seqlens.numel() - 1
+    host = None
+    if cu_seqlens_host is not None:
+        host = (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu_seqlens_host])
+    _check(lib().ea_hybrid_attn_prefill_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), dtype_code(q.dtype), _ptr(cu_seqlens), host, batch,
+        max_seqlen, q.shape[1], k.shape[1], q.shape[2], _ptr(route_bits), sink, window,
+        float(scale), _ptr(lse_out), _ptr(worklist_out), _capacity(worklist_out),
+        _stream(stream)))
 
 
 def hybrid_attn_run(q, k, v, o, cu_seqlens, max_seqlen, route_bits, sink, window, worklist,

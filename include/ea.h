@@ -152,6 +152,27 @@ ea_status ea_hybrid_attn_prefill(const void* q, const void* k, const void* v, vo
                                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * ea_hybrid_attn_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same arguments
+ * without workspace / ws_bytes, and the same kernels and results.  The queue counters and
+ * the internal work list live in a device array of the library (4 MiB per GPU, held until
+ * the process ends), whose address is taken once per device; the call allocates nothing.
+ * Limit: batch * n_heads_q * ceil(max_seqlen / 64) <= 262128 work items (EA_ERR_UNSUPPORTED
+ * beyond it; e.g. 32 heads x 256K tokens x 2 sequences fits).  Every call on one GPU shares
+ * the array: calls that overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Each call's planner resets what the attention kernel
+ * reads, so nothing an earlier call left there is used.
+ */
+ea_status ea_hybrid_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o,
+                                         ea_dtype dt, const int32_t* cu_seqlens,
+                                         const int32_t* cu_seqlens_host, int32_t batch,
+                                         int32_t max_seqlen, int32_t n_heads_q,
+                                         int32_t n_heads_kv, int32_t head_dim,
+                                         const uint8_t* route, int32_t sink, int32_t window,
+                                         float scale, float* lse_out, int32_t* worklist_out,
+                                         int64_t worklist_capacity, void* stream);
+
+/*
  * Chunked prefill over a KV prefix: the same routed attention when each sequence's queries
  * are only its newest tokens.  Sequence b has Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b]
  * positions whose keys and values are k, v [Tk, n_heads_kv, head_dim] (an earlier prefix,
