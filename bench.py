@@ -38,7 +38,10 @@ sys.path.insert(0, ROOT)
 
 from full_attention_long_amd import ea, inputs, metrics  # noqa: E402
 
-METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), 32K"
+METRIC = "hybrid-attn prefill ms/layer + effective TFLOP/s (% bf16 MFMA peak), {}"
+WORKLOAD_LABEL = {"qwen3_8b_32k": "32K", "llama8b_8k": "8K (Llama-3.1-8B-shaped)",
+                  "ragged4": "ragged 4-sequence batch", "long_256k": "256K",
+                  "tiny_fp32": "tiny fp32"}
 CHUNK_METRIC = "hybrid-attn chunked prefill (4K chunk over a 28K prefix) effective TFLOP/s"
 BACKWARD_METRIC = "hybrid-attn training backward (router STE + dq/dk/dv) effective TFLOP/s"
 DECODE_METRIC = "hybrid-attn decode step: cache GB/s (% HBM peak), 16 x 32K"
@@ -151,6 +154,36 @@ def copy_calibration():
     torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def settle(fn, seconds):
+    """Run fn until `seconds` of wall time have passed (at least once): untimed work before
+    the warm-up steps that brings the shader clock to its loaded steady state (the first
+    launches of a fresh process run up to 25% slower while it ramps).  Returns the count."""
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+    return n
+
+
+def time_events_evict(fn, n, scratch):
+    """Average ms of fn() over n calls, each timed alone with HIP events after a write of
+    the whole `scratch` buffer (512 MiB: the 256 MiB MALL and the 8 x 4 MiB L2 hold none of
+    the step's inputs when it starts); the write itself is not timed."""
+    total = 0.0
+    for _ in range(n):
+        if scratch is not None:
+            scratch.fill_(1.0)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        total += s.elapsed_time(e)
+    return total / n
 
 
 def time_events(fn, n):
@@ -543,6 +576,15 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="default qwen3_8b_32k (prefill) or decode_qwen3_8b_32k (decode)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="untimed steps before the warm-up steps, until this much wall time "
+                         "has passed (the shader clock ramps over the first launches)")
+    ap.add_argument("--alone", action="store_true",
+                    help="prefill: time every step alone (synchronised before it), no eviction "
+                         "write: the reference for --evict")
+    ap.add_argument("--evict", action="store_true",
+                    help="prefill: write a 512 MiB scratch buffer before each timed step and "
+                         "time every step alone (cold L2 / MALL); default: back-to-back steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one elementwise copy kernel of 1 GiB in and 1 GiB "
@@ -576,14 +618,20 @@ def main():
     torch.cuda.synchronize()
     n_sparse = int(layer.route.sum().item())
     F = layer.flops()
+    n_settle = settle(layer.step, args.settle_seconds)
     for _ in range(args.warmup):
         layer.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms = time_events(layer.step, args.steps)
+    if args.evict or args.alone:
+        scratch = torch.empty(1 << 27, dtype=torch.float32, device="cuda") if args.evict else None
+        ms = time_events_evict(layer.step, args.steps, scratch)
+    else:
+        ms = time_events(layer.step, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.3f} s)")
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.3f} s, after {n_settle} "
+        f"settle steps)")
 
     # phase breakdown and the attention kernel alone (same stream)
     ms_route = time_events(layer.do_route, args.steps) if layer.router is not None else 0.0
@@ -595,7 +643,7 @@ def main():
     peak = metrics.MI355X_BF16_DENSE_TFLOPS
     value = F / (ms * 1e-3) / 1e12
     rec = {
-        "metric": METRIC,
+        "metric": METRIC.format(WORKLOAD_LABEL.get(w.name, w.name)),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -614,6 +662,9 @@ def main():
                    "routing": "router" if w.router else f"bernoulli({w.p_sparse})"},
         "pct_bf16_peak": round(100.0 * value / peak, 2),
         "effective_tflop": round(F / 1e12, 4),
+        "settle_steps": n_settle,
+        "timing": ("each step alone after a 512 MiB eviction write" if args.evict
+                   else "each step alone" if args.alone else "back-to-back steps"),
         "ms_breakdown": {"route": round(ms_route, 4), "plan": round(ms_plan, 4),
                          "attention": round(ms_attn, 4)},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128>",
