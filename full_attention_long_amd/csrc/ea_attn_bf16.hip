@@ -279,10 +279,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[j][r] = 0.f;
 
-    // GEMM phase X(t): O^T += V(t-1)^T P(t-1)^T, then S^T(t) = K(t) Q^T, as 8 stages of 4
-    // MFMAs.  The LDS operands of stage i+1 are read during stage i (sched_barrier keeps
-    // the compiler from sinking the reads next to their MFMAs), so one wavefront keeps
-    // the matrix core busy on its own while its partner wavefront runs the softmax.
+    // GEMM phase X(t): O^T += V(t-1)^T P(t-1)^T, then S^T(t) = K(t) Q^T: 8 stages of KH
+    // MFMAs, 4 KH operands read from LDS.  Operand i is read RING - 1 MFMAs before the MFMA
+    // that uses it, into a ring of RING registers; sched_barrier after every MFMA keeps each
+    // read where it is issued, so the LDS reads trickle in one per MFMA rather than in
+    // bursts, and one wavefront keeps the matrix core busy on its own while its partner
+    // wavefront runs the softmax.  (A ring of 4 ran about 1% faster than reading a whole
+    // stage ahead in bursts, bit-identical; rings of 5 to 8 were no better.)
     // pv / qk: std::true_type or std::false_type (which of the two products to run)
     auto gemm_phase = [&](int t, auto pv, auto qk) __attribute__((always_inline)) {
       constexpr bool do_pv = decltype(pv)::value, do_qk = decltype(qk)::value;
@@ -290,65 +293,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       const unsigned char* kb = kbase + (t & 1) * S::TILE_BYTES;
       constexpr int KH = S::KSTEPS / 2;
       static_assert(S::DT == KH, "stages hold DT V operands or KSTEPS/2 K operands");
-      // stage c < 4: V^T operands of 16-key slice (j, kh) = (c / 2, c % 2), all column
-      // tiles (P keys 32j + 16kh + 8(e/4) + 4g + e%4); stage c >= 4: K operands of
-      // sub-tile j = (c - 4) / 2, k-steps KH*((c - 4) % 2) + [0, KH).
-      auto read_ops = [&](int c, bf16x8 (&op)[KH]) __attribute__((always_inline)) {
+      constexpr int RING = 4;
+      // operand i = KH c + q of stage c: for c < 4 the V^T operand of column tile q and
+      // 16-key slice (j, kh) = (c / 2, c % 2) (P keys 32j + 16kh + 8(e/4) + 4g + e%4), read
+      // transposed from the row-major V tile; for c >= 4 the K operand of sub-tile
+      // j = (c - 4) / 2, k-step KH ((c - 4) % 2) + q
+      auto read1 = [&](int i, bf16x8& o) __attribute__((always_inline)) {
+        const int c = i / KH, q = i % KH;
         if (c < 4) {
           const int j = c / 2, kh = c % 2;
           const int row = 32 * j + 16 * kh + tr_row;
-#pragma unroll
-          for (int dt = 0; dt < S::DT; ++dt) {
-            const int col = 32 * dt + tr_col;  // element column; rows row and row + 8
-            const unsigned char* p0 =
-                vb + row * S::ROW_BYTES + (((col / 8) ^ S::swz_v(row)) * 16) + (col % 8) * 2;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-            const s16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::ROW_BYTES));
-            op[dt] = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
+          const int col = 32 * q + tr_col;  // element column; rows row and row + 8
+          const unsigned char* p0 =
+              vb + row * S::ROW_BYTES + (((col / 8) ^ S::swz_v(row)) * 16) + (col % 8) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::ROW_BYTES));
+          o = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
           const int j = (c - 4) / 2, k0 = KH * ((c - 4) % 2);
           const int row = 32 * j + l32;
-#pragma unroll
-          for (int q = 0; q < KH; ++q)
-            op[q] = *(const bf16x8*)(kb + row * S::ROW_BYTES +
-                                     (((2 * (k0 + q) + g) ^ S::swz_k(row)) * 16));
+          o = *(const bf16x8*)(kb + row * S::ROW_BYTES +
+                               (((2 * (k0 + q) + g) ^ S::swz_k(row)) * 16));
         }
       };
-      // sacc[j][r] = score(key kt*BN + 32j + 8(r/4) + 4g + r%4, query qi)
-      auto run_ops = [&](int c, const bf16x8 (&op)[KH]) __attribute__((always_inline)) {
+      // sacc[j][r] = score(key kt*BN + 32j + 8(r/4) + 4g + r%4, query qi); the row sums of
+      // each 16-key slice of P run on the matrix core after its last P V MFMA
+      auto run1 = [&](int i, const bf16x8& o) __attribute__((always_inline)) {
+        const int c = i / KH, q = i % KH;
         if (c < 4) {
           const int j = c / 2, kh = c % 2;
-#pragma unroll
-          for (int dt = 0; dt < S::DT; ++dt)
-            oacc[dt] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[dt], pb[j][kh], oacc[dt], 0, 0, 0);
-          lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, pb[j][kh], lacc, 0, 0, 0);
+          oacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, pb[j][kh], oacc[q], 0, 0, 0);
+          if (q == KH - 1)
+            lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, pb[j][kh], lacc, 0, 0, 0);
         } else {
           const int j = (c - 4) / 2, k0 = KH * ((c - 4) % 2);
-          if (k0 == 0)
+          if (k0 == 0 && q == 0)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[j][r] = 0.f;
-#pragma unroll
-          for (int q = 0; q < KH; ++q)
-            sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[q], qreg[k0 + q], sacc[j], 0, 0, 0);
+          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o, qreg[k0 + q], sacc[j], 0, 0, 0);
         }
       };
-      constexpr int c0 = do_pv ? 0 : 4, c1 = do_qk ? 8 : 4;
-      bf16x8 opa[KH], opb[KH];
-      read_ops(c0, opa);
+      constexpr int i0 = (do_pv ? 0 : 4) * KH, i1 = (do_qk ? 8 : 4) * KH;
+      bf16x8 ring[RING];
+#pragma unroll
+      for (int m = 0; m < RING - 1; ++m)
+        if (i0 + m < i1) read1(i0 + m, ring[m]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 8; c += 2) {
-        if (c < c0 || c >= c1) continue;
-        if (c + 1 < c1) read_ops(c + 1, opb);
-        run_ops(c, opa);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 >= c1) break;
-        if (c + 2 < c1) read_ops(c + 2, opa);
-        run_ops(c + 1, opb);
+      for (int i = i0; i < i1; ++i) {
+        if (i + RING - 1 < i1) read1(i + RING - 1, ring[(i - i0 + RING - 1) % RING]);
+        run1(i, ring[(i - i0) % RING]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
