@@ -269,40 +269,29 @@ __global__ __launch_bounds__(kThreadsDkv, 1) void bwd_dkv_mfma(BwdArgs a) {
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
-      // A: one k-step per group (S and dP), the four operands read one group ahead
-      auto readA = [&](int ks, bf16x8 (&op)[4]) {
-        op[0] = read_plain<D>(qb, 32 * j, ks, l32, g);
-        op[1] = read_plain<D>(gb, 32 * j, ks, l32, g);
-        op[2] = read_plain<D>(kvk, 32 * kb, ks, l32, g);  // K^T: lane holds key l32's dims
-        op[3] = read_plain<D>(kvv, 32 * kb, ks, l32, g);
-      };
-      auto runA = [&](const bf16x8 (&op)[4]) {
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], op[2], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[1], op[3], pacc, 0, 0, 0);
-      };
-      auto readC = [&](int c, bf16x8 (&op)[4]) {
-        const int kh = c / O::HALF, dt0 = 2 * (c % O::HALF);
-        op[0] = read_tr<D>(gb, 32 * j + 16 * kh, dt0, tr_row, tr_col);
-        op[1] = read_tr<D>(qb, 32 * j + 16 * kh, dt0, tr_row, tr_col);
-        op[2] = read_tr<D>(gb, 32 * j + 16 * kh, dt0 + 1, tr_row, tr_col);
-        op[3] = read_tr<D>(qb, 32 * j + 16 * kh, dt0 + 1, tr_row, tr_col);
-      };
       bf16x8 pb[2], db[2];
-      auto runC = [&](int c, const bf16x8 (&op)[4]) {
-        const int kh = c / O::HALF, dt0 = 2 * (c % O::HALF);
-        dv[dt0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], pb[kh], dv[dt0], 0, 0, 0);
-        dk[dt0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[1], db[kh], dk[dt0], 0, 0, 0);
-        dv[dt0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[2], pb[kh], dv[dt0 + 1], 0, 0, 0);
-        dk[dt0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[3], db[kh], dk[dt0 + 1], 0, 0, 0);
-      };
+      // A: S += Q K^T and dP += dO V^T, one MFMA per k-step and product; each MFMA's two
+      // operands are read RA - 1 MFMAs ahead into a ring (one pair per MFMA, not in bursts)
       {
-        bf16x8 op[2][4];
-        readA(0, op[0]);
+        constexpr int NA2 = 2 * S::KSTEPS, RA = 3;
+        // MFMA m: S (Q rows, K^T: lane holds key l32's dims) for even m, dP (dO, V) for odd,
+        // k-step m / 2
+        auto rdA = [&](int m, bf16x8 (&o)[2]) __attribute__((always_inline)) {
+          const int ks = m / 2;
+          o[0] = read_plain<D>(m % 2 == 0 ? qb : gb, 32 * j, ks, l32, g);
+          o[1] = read_plain<D>(m % 2 == 0 ? kvk : kvv, 32 * kb, ks, l32, g);
+        };
+        bf16x8 ra[RA][2];
+#pragma unroll
+        for (int m = 0; m < RA - 1; ++m) rdA(m, ra[m]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < S::KSTEPS; ++ks) {
-          if (ks + 1 < S::KSTEPS) readA(ks + 1, op[(ks + 1) & 1]);
-          runA(op[ks & 1]);
+        for (int m = 0; m < NA2; ++m) {
+          if (m + RA - 1 < NA2) rdA(m + RA - 1, ra[(m + RA - 1) % RA]);
+          if (m % 2 == 0)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % RA][0], ra[m % RA][1], sacc, 0, 0, 0);
+          else
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[m % RA][0], ra[m % RA][1], pacc, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -336,13 +325,31 @@ __global__ __launch_bounds__(kThreadsDkv, 1) void bwd_dkv_mfma(BwdArgs a) {
       else
         phase_b(std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
-      // C: single-buffered operands (the partner wavefront on the SIMD covers the latency)
+      // C: dV^T += dO^T P and dK^T += Q^T dS for 16-row slice kh and column tile dt; MFMA m is
+      // (kh, dt) = (c / HALF, 2 (c % HALF) + w / 2) with c = m / 4, w = m % 4, dV for even w;
+      // its transposed operand is read RC - 1 MFMAs ahead into a ring
+      {
+        constexpr int NC4 = 4 * O::NC, RC = 6;
+        auto rdC = [&](int m, bf16x8& o) __attribute__((always_inline)) {
+          const int c = m / 4, w = m % 4;
+          const int kh = c / O::HALF, dt0 = 2 * (c % O::HALF);
+          o = read_tr<D>(w % 2 == 0 ? gb : qb, 32 * j + 16 * kh, dt0 + w / 2, tr_row, tr_col);
+        };
+        bf16x8 rc[RC];
 #pragma unroll
-      for (int c = 0; c < O::NC; ++c) {
-        bf16x8 op[4];
-        readC(c, op);
-        runC(c, op);
+        for (int m = 0; m < RC - 1; ++m) rdC(m, rc[m]);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NC4; ++m) {
+          if (m + RC - 1 < NC4) rdC(m + RC - 1, rc[(m + RC - 1) % RC]);
+          const int c = m / 4, w = m % 4;
+          const int kh = c / O::HALF, dt = 2 * (c % O::HALF) + w / 2;
+          if (w % 2 == 0)
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rc[m % RC], pb[kh], dv[dt], 0, 0, 0);
+          else
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rc[m % RC], db[kh], dk[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // the next stage's loads (this wavefront's share) have landed; after the barrier every
