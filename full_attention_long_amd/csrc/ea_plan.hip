@@ -34,8 +34,10 @@ struct HeadMask {
 };
 
 // Cell i: {seq, q_tile, cost, mode mask (1 = full heads, 2 = sparse heads)}; cost 0 = empty.
+// len_of[b] = chunk rows of sequence b, off_of[b] = position of its chunk row 0 (keys - rows).
 __device__ __forceinline__ int4 make_cell(int i, const PlanArgs& a, const int* qt_prefix,
-                                          const int* n_sparse_of) {
+                                          const int* n_sparse_of, const int* len_of,
+                                          const int* off_of) {
   const int f = i >> 1, sub = i & 1;
   int lo = 0, hi = a.batch - 1;  // last b with qt_prefix[b] <= f (never an empty sequence)
   while (lo < hi) {
@@ -43,8 +45,8 @@ __device__ __forceinline__ int4 make_cell(int i, const PlanArgs& a, const int* q
     if (qt_prefix[mid] <= f) lo = mid; else hi = mid - 1;
   }
   const int b = lo, qt = f - qt_prefix[b];
-  const int len = a.cu[b + 1] - a.cu[b];
-  const int off = a.cu_k ? (a.cu_k[b + 1] - a.cu_k[b]) - len : 0;  // position of chunk row 0
+  const int len = len_of[b];
+  const int off = off_of[b];
   if (off < 0) return int4{b, qt, 0, 0};  // keys shorter than the chunk: no items
   const int m0 = off + qt * a.bm, m1 = off + min(qt * a.bm + a.bm, len);
   const int t_hi = (m1 - 1) / a.bn;
@@ -107,15 +109,24 @@ __device__ void empty_list(const PlanArgs& a) {
 // every item, and the total), slot_base (first slot of a split item, else -1), split_list and
 // counters[3] (pieces), counters[4] (split items).  The list order is unchanged, so the pieces
 // of one item are consecutive and long items still come first.
-__device__ void split_phase(const PlanArgs& a, int n_items, int* scratch) {
+__device__ void split_phase(const PlanArgs& a, int n_items, int* scratch, const uint64_t* cells,
+                            const int* cell_off, int n_valid) {
   __shared__ unsigned long long s_sum;
   __shared__ int s_slots;
   const int tid = threadIdx.x;
-  __syncthreads();  // the items written in phase 5 are visible to the whole workgroup
+  // the cost of item i: that of the sorted cell holding it (the last p with cell_off[p] <= i)
+  auto cost_of = [&](int i) {
+    int lo = 0, hi = n_valid - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cell_off[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return (int)((cells[lo] >> 2) & 0x3fffff);
+  };
   if (tid == 0) s_sum = 0;
   __syncthreads();
   unsigned long long part = 0;
-  for (int i = tid; i < n_items; i += kPlanThreads) part += (unsigned)a.items[i].w;
+  for (int i = tid; i < n_items; i += kPlanThreads) part += (unsigned)cost_of(i);
   atomicAdd(&s_sum, part);
   __syncthreads();
   const long long total = (long long)s_sum;
@@ -130,7 +141,7 @@ __device__ void split_phase(const PlanArgs& a, int n_items, int* scratch) {
     __syncthreads();
     int slots = 0;
     for (int i = tid; i < n_items; i += kPlanThreads) {
-      const int ns = pieces_of(a.items[i].w);
+      const int ns = pieces_of(cost_of(i));
       if (ns > 1) slots += ns;
     }
     atomicAdd(&s_slots, slots);
@@ -143,7 +154,7 @@ __device__ void split_phase(const PlanArgs& a, int n_items, int* scratch) {
   int carry_p = 0, carry_s = 0, carry_n = 0;
   for (int base = 0; base < n_items; base += kPlanThreads) {
     const int i = base + tid;
-    const int ns = i < n_items ? pieces_of(a.items[i].w) : 0;
+    const int ns = i < n_items ? pieces_of(cost_of(i)) : 0;
     const int sl = ns > 1 ? ns : 0;
     int tp, ts, tn;
     const int ep = block_exclusive_scan(ns, &tp, scratch);
@@ -171,6 +182,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ HeadMask masks[kPlanMaxBatch];    // sparse heads of every sequence
   __shared__ int qt_prefix[kPlanMaxBatch + 1]; // first slot of every sequence
   __shared__ int n_sparse_of[kPlanMaxBatch];
+  __shared__ int len_of[kPlanMaxBatch];        // chunk rows of every sequence
+  __shared__ int off_of[kPlanMaxBatch];        // position of its chunk row 0 (keys - rows)
   __shared__ int scratch[kNumWaves + 1];
   __shared__ int s_valid;
   const int tid = threadIdx.x;
@@ -194,7 +207,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int b = base + tid;
     int nq = 0;
     if (b < B) {
-      nq = ceil_div(a.cu[b + 1] - a.cu[b], a.bm);
+      const int len = a.cu[b + 1] - a.cu[b];
+      len_of[b] = len;
+      off_of[b] = a.cu_k ? (a.cu_k[b + 1] - a.cu_k[b]) - len : 0;
+      nq = ceil_div(len, a.bm);
       n_sparse_of[b] = __popcll(masks[b].lo) + __popcll(masks[b].hi);
     }
     int tot;
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int i = tid; i < n_pad; i += kPlanThreads) {
     uint64_t key = ~0ull;
     if (i < n_cells) {
-      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of);
+      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of, len_of, off_of);
       if (c.z > 0) {
         key = ((uint64_t)(0x7fffffff - c.z) << 32) | (uint32_t)i;
         atomicAdd(&s_valid, 1);
@@ -227,7 +243,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  // Phase 3: bitonic sort, ascending.
+  // Phase 3: bitonic sort, ascending.  Up to one key per thread, each thread keeps its key
+  // in registers and takes its partner's by a wavefront shuffle when the partner is in the
+  // same wavefront (distance < 64), through LDS otherwise; element i keeps the smaller of
+  // the pair when it is the lower index of an ascending pair or the higher of a descending
+  // one, the larger otherwise (the compare-exchange, computed on both sides).
+  if (n_pad <= kPlanThreads) {
+    uint64_t v = tid < n_pad ? keys[tid] : ~0ull;
+    for (int k = 2; k <= n_pad; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint64_t y;
+        if (j < 64) {
+          const unsigned lo = __shfl_xor((unsigned)v, j, 64);
+          const unsigned hi = __shfl_xor((unsigned)(v >> 32), j, 64);
+          y = ((uint64_t)hi << 32) | lo;
+        } else {
+          keys[tid] = v;
+          __syncthreads();
+          y = keys[tid ^ j];
+          __syncthreads();
+        }
+        const bool keep_min = ((tid & k) == 0) == ((tid & j) == 0);
+        v = keep_min ? (v < y ? v : y) : (v < y ? y : v);
+      }
+    }
+    if (tid < n_pad) keys[tid] = v;
+    __syncthreads();
+  } else
   for (int k = 2; k <= n_pad; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < n_pad; i += kPlanThreads) {
@@ -253,7 +295,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int sz = 0;
     if (p < n_valid) {
       const int i = (int)(keys[p] & 0xffffffffu);
-      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of);
+      const int4 c = make_cell(i, a, qt_prefix, n_sparse_of, len_of, off_of);
       const int ns = n_sparse_of[c.x];
       sz = ((c.w & 1) ? Hq - ns : 0) + ((c.w & 2) ? ns : 0);
       // packed cell: seq (20 bits) | q_tile (20 bits) | cost (22 bits) | mode (2 bits)
@@ -290,7 +332,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     a.counters[2] = 0;  // workgroups finished
     if (a.n_items_out) *a.n_items_out = items_total;
   }
-  if (a.split_workers > 0) split_phase(a, items_total, scratch);
+  if (a.split_workers > 0) split_phase(a, items_total, scratch, keys, cell_off, n_valid);
 }
 
 }  // namespace
