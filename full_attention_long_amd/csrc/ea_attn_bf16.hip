@@ -557,8 +557,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 // Merge of a split item's pieces: for each of its rows, M = max of the pieces' reference
 // maxima, w_p = 2^((m_p - M) * scale * log2 e), O = sum_p O_p w_p / sum_p l_p w_p (fp32, one
 // bf16 rounding), LSE = M * scale + ln sum_p l_p w_p.  One workgroup per (split item, block
-// of kCombineRows rows); a thread takes 4 head dimensions of a row.
-constexpr int kCombineRows = 32;
+// of 256 / (D / 4) rows); a thread takes 4 head dimensions of one row and issues the loads
+// of every piece before the first use (one memory round trip for the maxima and sums, one
+// for the partial outputs), then adds the pieces in order.
+template <int D>
+constexpr int combine_rows() { return 256 / (D / 4); }
 template <int D>
 __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, const int32_t* split_list,
                                                             const int32_t* n_split) {
@@ -571,33 +574,45 @@ __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, const in
   const int seq0 = a.cu[b];
   const int len = a.cu[b + 1] - seq0;
   const int r0 = qt * BM, nrows = min(BM, len - r0);
-  const int rbeg = rblk * kCombineRows, rend = min(nrows, rbeg + kCombineRows);
-  const int ns = a.piece_prefix[it + 1] - a.piece_prefix[it];
+  constexpr int C4 = D / 4;
+  const int c = threadIdx.x % C4;
+  const int r = rblk * combine_rows<D>() + threadIdx.x / C4;
+  if (r >= nrows) return;
+  const int ns = min(a.piece_prefix[it + 1] - a.piece_prefix[it], kSplitMaxPieces);
   const int64_t slot0 = a.slot_base[it];
   const int total_tokens = a.cu[a.batch];
   const float c_log2 = a.scale * 1.4426950408889634f;
-  constexpr int C4 = D / 4, RPP = 256 / C4;
-  const int c = threadIdx.x % C4;
-  for (int r = rbeg + threadIdx.x / C4; r < rend; r += RPP) {
-    float M = -INFINITY;
-    for (int p = 0; p < ns; ++p) M = fmaxf(M, a.ml_part[((slot0 + p) * BM + r) * 2]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float l = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < ns; ++p) {
-      const float m = a.ml_part[((slot0 + p) * BM + r) * 2];
-      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - Mu) * c_log2);
-      l += a.ml_part[((slot0 + p) * BM + r) * 2 + 1] * w;
-      acc += w * *(const f32x4*)(a.o_part + ((slot0 + p) * BM + r) * D + 4 * c);
+  float mp[kSplitMaxPieces], lp[kSplitMaxPieces];
+  f32x4 op[kSplitMaxPieces];
+#pragma unroll
+  for (int p = 0; p < kSplitMaxPieces; ++p)
+    if (p < ns) {
+      mp[p] = a.ml_part[((slot0 + p) * BM + r) * 2];
+      lp[p] = a.ml_part[((slot0 + p) * BM + r) * 2 + 1];
+      op[p] = *(const f32x4*)(a.o_part + ((slot0 + p) * BM + r) * D + 4 * c);
     }
-    const float inv = 1.0f / l;
-    __bf16* o = (__bf16*)a.o + ((int64_t)(seq0 + r0 + r) * Hq + h) * D + 4 * c;
-    u32x2 wv;
-    wv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    wv[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-    *(u32x2*)o = wv;
-    if (a.lse && c == 0) a.lse[(int64_t)h * total_tokens + seq0 + r0 + r] = Mu * a.scale + logf(l);
-  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kSplitMaxPieces; ++p)
+    if (p < ns) M = fmaxf(M, mp[p]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < kSplitMaxPieces; ++p)
+    if (p < ns) {
+      const float m = mp[p];
+      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - Mu) * c_log2);
+      l += lp[p] * w;
+      acc += w * op[p];
+    }
+  const float inv = 1.0f / l;
+  __bf16* o = (__bf16*)a.o + ((int64_t)(seq0 + r0 + r) * Hq + h) * D + 4 * c;
+  u32x2 wv;
+  wv[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  wv[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)o = wv;
+  if (a.lse && c == 0) a.lse[(int64_t)h * total_tokens + seq0 + r0 + r] = Mu * a.scale + logf(l);
 }
 
 }  // namespace
@@ -606,12 +621,13 @@ int attn_bf16_blocks_per_cu() { return 1; }
 
 hipError_t launch_split_combine(const AttnArgs& a, const int32_t* split_list,
                                 const int32_t* n_split, hipStream_t stream) {
-  // at most kSplitSlots / 2 split items (each has >= 2 pieces), BM / kCombineRows row blocks
-  const dim3 grid(kSplitSlots / 2, BM / kCombineRows);
+  // at most kSplitSlots / 2 split items (each has >= 2 pieces), BM / combine_rows row blocks
   if (a.head_dim == 128)
-    split_combine_kernel<128><<<grid, 256, 0, stream>>>(a, split_list, n_split);
+    split_combine_kernel<128><<<dim3(kSplitSlots / 2, BM / combine_rows<128>()), 256, 0, stream>>>(
+        a, split_list, n_split);
   else
-    split_combine_kernel<64><<<grid, 256, 0, stream>>>(a, split_list, n_split);
+    split_combine_kernel<64><<<dim3(kSplitSlots / 2, BM / combine_rows<64>()), 256, 0, stream>>>(
+        a, split_list, n_split);
   return hipGetLastError();
 }
 

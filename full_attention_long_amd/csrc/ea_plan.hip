@@ -314,16 +314,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     return;
   }
 
-  // Phase 5: expansion, heads of a cell in ascending order.
-  for (int p = tid; p < n_valid; p += kPlanThreads) {
-    const uint64_t pk = keys[p];
-    const int b = (int)(pk >> 44), qt = (int)((pk >> 24) & 0xfffff);
-    const int cost = (int)((pk >> 2) & 0x3fffff), mode = (int)(pk & 3);
-    const HeadMask m = masks[b];
-    int at = cell_off[p];
-    for (int h = 0; h < Hq; ++h) {
-      const bool sp = ((h < 64 ? (m.lo >> h) : (m.hi >> (h - 64))) & 1ull) != 0;
-      if (mode & (sp ? 2 : 1)) a.items[at++] = int4{b, h, qt, cost};
+  // Phase 5: expansion, heads of a cell in ascending order.  Each cell's heads are cut into
+  // 2^ls runs of `per` heads, as many as keep every thread busy, and one thread writes a run:
+  // its first item goes to the cell's offset plus the number of the cell's heads below the
+  // run (all of them for a cell of both modes, else the sparse or the full ones, by
+  // popcount).
+  {
+    int ls = 0;
+    while ((1 << ls) < Hq && n_valid * (2 << ls) <= kPlanThreads) ++ls;
+    const int per = (Hq + (1 << ls) - 1) >> ls;
+    for (int x = tid; x < (n_valid << ls); x += kPlanThreads) {
+      const int p = x >> ls, hb = (x & ((1 << ls) - 1)) * per, he = min(Hq, hb + per);
+      if (hb >= he) continue;
+      const uint64_t pk = keys[p];
+      const int b = (int)(pk >> 44), qt = (int)((pk >> 24) & 0xfffff);
+      const int cost = (int)((pk >> 2) & 0x3fffff), mode = (int)(pk & 3);
+      const HeadMask m = masks[b];
+      const int sp_below = hb < 64 ? __popcll(m.lo & ((1ull << hb) - 1ull))
+                                   : __popcll(m.lo) + __popcll(m.hi & ((1ull << (hb - 64)) - 1ull));
+      int at = cell_off[p] + (mode == 3 ? hb : (mode == 2 ? sp_below : hb - sp_below));
+      for (int h = hb; h < he; ++h) {
+        const bool sp = ((h < 64 ? (m.lo >> h) : (m.hi >> (h - 64))) & 1ull) != 0;
+        if (mode & (sp ? 2 : 1)) a.items[at++] = int4{b, h, qt, cost};
+      }
     }
   }
   if (tid == 0) {
