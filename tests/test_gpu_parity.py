@@ -240,6 +240,22 @@ def test_prefill_random_configs(seed):
     check_case(q, k, v, lens, route, sink, window, what=f"random {seed}", strict=False)
 
 
+@pytest.mark.parametrize("hq,hkv,dtype", [(96, 8, torch.bfloat16), (128, 16, torch.bfloat16),
+                                           (128, 32, torch.float32)])
+def test_many_query_heads(hq, hkv, dtype):
+    """Query heads past 64 (the second word of the planner's per-sequence head masks, up to
+    its limit of 128): the work list bit for bit and every row, with both modes mixed."""
+    lens = [300, 1, 520]
+    q, k, v = rand_qkv(sum(lens), hq, hkv, 64, dtype, 77)
+    g = torch.Generator().manual_seed(5)
+    route = (torch.rand(len(lens), hq, generator=g) < 0.6).to(torch.uint8)
+    route[0, 70] = 0   # a full head and a sparse head past 64 in every configuration
+    route[0, 90] = 1
+    # rows with one to a few visible keys (the one-token sequence, a sequence's first rows)
+    # reach |o| > 2, where bf16 itself is coarser than 1e-2: the relative form of the bound
+    check_case(q, k, v, lens, route, 16, 128, what=f"hq {hq} {dtype}", strict=False)
+
+
 def test_worklist_route_run_share_a_workspace():
     """ea_build_worklist, then ea_route, then ea_hybrid_attn_run on one workspace: the
     router's scratch lies past the queue counters the run takes items through, so the run
