@@ -340,10 +340,11 @@ def test_backward_workload_32k_sampled():
     assert err_k <= 2e-3 and err_v <= 2e-3
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 4, 64), (8, 1, 128), (16, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 4, 64), (8, 1, 128), (16, 2, 64),
+                                      (96, 8, 64)])
 def test_backward_group_sizes(hq, hkv, d):
-    # one query head per KV head (dk, dv written directly, no partials) and large groups
-    # (partials of up to 8 heads summed in head order)
+    # one query head per KV head (dk, dv written directly, no partials), large groups
+    # (partials of up to 8 heads summed in head order) and 96 query heads
     lens = [333, 700, 65]
     g = torch.Generator().manual_seed(hq * 100 + hkv * 10 + d)
     route = (torch.rand(len(lens), hq, generator=g) < 0.5).to(torch.uint8)

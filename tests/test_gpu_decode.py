@@ -94,6 +94,22 @@ def test_decode_split_boundaries(dtype, d, G):
     check_decode(q, kc, vc, lens, route, 16, 200, f"splits d{d} G{G} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_many_query_heads(dtype):
+    """128 query heads on 16 KV heads (group 8, the kernel's largest), with full and sparse
+    heads past head 64 and an all-sparse group."""
+    hq, hkv, d, cap = 128, 16, 64, 1200
+    lens = [1, 300, 1100]
+    g = torch.Generator().manual_seed(4242)
+    q = torch.randn(len(lens), hq, d, generator=g).to(dtype)
+    kc = torch.randn(len(lens), cap, hkv, d, generator=g).to(dtype)
+    vc = torch.randn(len(lens), cap, hkv, d, generator=g).to(dtype)
+    route = (torch.rand(len(lens), hq, generator=g) < 0.6).to(torch.uint8)
+    route[2, 64:72] = 1   # an all-sparse group past head 64
+    route[2, 72] = 0      # and a full head in the next one
+    check_decode(q, kc, vc, lens, route, 16, 200, f"decode hq {hq} {dtype}")
+
+
 @pytest.mark.parametrize("sink,window", [(0, 1), (1, 1), (300, 5), (0, 2000), (64, 256)])
 def test_decode_sink_window_edges(sink, window):
     lens = [1, 5, 300, 301, 1024, 1800]
