@@ -160,6 +160,27 @@ def test_device_lengths_beyond_max_seqlen_give_an_empty_work_list():
     assert torch.all(o.float() == -12288.0)
 
 
+def test_chunked_many_query_heads():
+    """128 query heads on 16 KV heads, long enough that full-head items split: the planner's
+    split phase over many items (costs read from its sorted cells), every row and the work
+    list against the oracle."""
+    lens_k, lens_q = [2600, 900], [700, 900]
+    hq, hkv, d = 128, 16, 64
+    q, k, v, cu_q, cu_k = chunk_inputs(lens_k, lens_q, hq, hkv, d, torch.bfloat16, 4711)
+    g = torch.Generator().manual_seed(4712)
+    route = (torch.rand(len(lens_k), hq, generator=g) < 0.5).to(torch.uint8)
+    sink, window = 16, 256
+    say(f"case chunked hq {hq}: lens_k={lens_k} lens_q={lens_q} hkv={hkv} d={d}")
+    o, lse, items, bm = run_chunked(q, k, v, cu_q, cu_k, route, sink, window)
+    ro, rl = oracle.attn(q, k, v, cu_q, hq, hkv, route.numpy(), sink, window, cu_seqlens_k=cu_k)
+    H.compare(o, ro, torch.bfloat16, f"chunked hq {hq}", strict=False)
+    assert np.abs(lse.double().numpy().T - rl).max() <= 4e-3
+    _, bn = ea.tile_config(ea.dtype_code(torch.bfloat16), d)
+    want = oracle.worklist(route.numpy(), cu_q, hq, sink, window, bm, bn, cu_seqlens_k=cu_k)
+    assert np.array_equal(items[:len(want)], want)
+    assert np.all(items[len(want):] == -1)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_chunked_random_configs(seed):
     """Seeded random chunks: 1-4 sequences, key lengths from 1 to 2600, chunk lengths from
